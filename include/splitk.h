@@ -1,0 +1,126 @@
+/*
+ * splitk.h -- C ABI of the split-K GEMM library for AMD MI355X (gfx950).
+ *
+ * Operation (restated from "Aligned shared rows for pipelined NAX on CUDA",
+ * section "Contract and correctness", and "Wider consecutive-weight NAX
+ * GEMM", section "Launch contract and correctness"):
+ *
+ *   A is [M,K] and B is [N,K], both row-major (each row contiguous in k), with
+ *   elements of one type: F32, F16 or BF16.  B holds weights the caller has
+ *   prepared once and keeps resident; the library reads it in place and never
+ *   copies, packs or transposes it ("Performance method" of the second page).
+ *   The K axis is cut into `splits` slices: slice s is
+ *   [s*k_per_split, min((s+1)*k_per_split, K)).  Every slice starts below K,
+ *   together they cover K, and only the last one may be shorter.
+ *
+ *   splitk_gemm_bt:  partials[s,i,j] = sum_{k in slice s} A[i,k] * B[j,k]
+ *                    (F32 result; F16/BF16 products use the matrix cores'
+ *                    native F16/BF16 inputs with F32 accumulation).
+ *   splitk_reduce:   C[i,j] = sum_{s=0}^{splits-1} partials[s,i,j]
+ *                    (F32, slabs added in ascending s).
+ *   splitk_gemm_bt_reduce: the two above, back to back on one stream.
+ *
+ * Shape domain (same sections): M, K and k_per_split are positive multiples
+ * of 32 and N is a positive multiple of 64.  Inputs have exactly the stated
+ * extents -- the library never reads past A[M*K] or B[N*K] and never writes
+ * outside partials[splits*M*N] or C[M*N] -- and outputs are separate storage
+ * that aliases nothing else.
+ *
+ * Layout of every buffer is dense row-major: A[M][K], B[N][K],
+ * partials[splits][M][N] (slab stride M*N floats), C[M][N].
+ *
+ * Pointers are device pointers (HIP device memory of the current device);
+ * `stream` is a hipStream_t (NULL = the legacy default stream).  The caller
+ * owns and frees every buffer; the library allocates nothing, keeps no state
+ * between calls and is safe to call from several threads.
+ *
+ * Errors: arguments are checked on the host before anything is enqueued; a
+ * non-zero status means nothing was launched.  SPLITK_OK means the kernels
+ * were enqueued on `stream`; execution is asynchronous and a device fault
+ * would surface at the caller's next synchronisation.  There is no host
+ * synchronisation, allocation or stream query inside, so the calls may be
+ * captured into a HIP graph.  On success every element of partials (and of C)
+ * is overwritten; nothing past their ends is touched.
+ */
+#ifndef SPLITK_H
+#define SPLITK_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SPLITK_F32 = 0,
+    SPLITK_F16 = 1,
+    SPLITK_BF16 = 2
+} splitk_dtype;
+
+typedef enum {
+    SPLITK_OK = 0,
+    SPLITK_ERR_NULL = 1,   /* a required pointer is NULL                            */
+    SPLITK_ERR_DTYPE = 2,  /* dtype is not one of splitk_dtype                      */
+    SPLITK_ERR_SHAPE = 3,  /* M, K, k_per_split not positive multiples of 32, or N  */
+                           /* not a positive multiple of 64                         */
+    SPLITK_ERR_SPLIT = 4,  /* splits < 1, a slice starting at or past K, or the     */
+                           /* slices not covering K                                 */
+    SPLITK_ERR_ALIAS = 5,  /* an output overlaps an input or the other output       */
+    SPLITK_ERR_ALIGN = 6,  /* a base pointer is not 16-byte aligned                 */
+    SPLITK_ERR_RANGE = 7,  /* a buffer holds 2^31 elements or more                  */
+    SPLITK_ERR_LAUNCH = 8  /* the HIP runtime refused the launch                    */
+} splitk_status;
+
+/*
+ * Split-K GEMM into F32 partial slabs (first page, "Contract and
+ * correctness"; second page, "Launch contract and correctness").
+ *   A         [M,K] elements of `dtype`, read only.
+ *   B         [N,K] elements of `dtype`, read only, resident weights.
+ *   partials  [splits,M,N] F32, written in full (no accumulation into it).
+ *   dtype     a splitk_dtype value.
+ * Returns a splitk_status.
+ */
+int splitk_gemm_bt(const void* A, const void* B, float* partials, int64_t M, int64_t N, int64_t K,
+                   int64_t k_per_split, int64_t splits, int dtype, void* stream);
+
+/*
+ * The separate accumulation pass that turns the slabs into the final output
+ * (first page, "Contract and correctness" and "Measurement protocol"; second
+ * page, "Performance method").
+ *   partials  [splits,M,N] F32, read only; `splits` must be the value that
+ *             produced them.
+ *   C         [M,N] F32, written in full.
+ * M must be a positive multiple of 32 and N of 64, as for the GEMM.
+ * Returns a splitk_status.
+ */
+int splitk_reduce(const float* partials, float* C, int64_t splits, int64_t M, int64_t N,
+                  void* stream);
+
+/*
+ * Complete operation: splitk_gemm_bt then splitk_reduce on the same stream,
+ * the chain the pages time as one captured graph (first page, "Measurement
+ * protocol").  Arguments as above; all of them are checked before either
+ * kernel is enqueued, and C must not overlap partials, A or B.
+ */
+int splitk_gemm_bt_reduce(const void* A, const void* B, float* partials, float* C, int64_t M,
+                          int64_t N, int64_t K, int64_t k_per_split, int64_t splits, int dtype,
+                          void* stream);
+
+/* Static text for a status code ("unknown status" for anything else). */
+const char* splitk_status_str(int status);
+
+/*
+ * Describes, without launching anything, the GEMM kernel configuration the
+ * library would use for these arguments: writes a NUL-terminated text such as
+ * "wavek bm32 bn64 waves4 grid256" into buf (at most `len` bytes, truncated).
+ * Returns a splitk_status from the same argument checks as splitk_gemm_bt,
+ * minus the pointer checks.
+ */
+int splitk_describe(int64_t M, int64_t N, int64_t K, int64_t k_per_split, int64_t splits,
+                    int dtype, char* buf, int64_t len);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPLITK_H */

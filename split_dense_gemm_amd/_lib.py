@@ -1,0 +1,162 @@
+"""ctypes binding of libsplitk.so (argument marshalling only).
+
+Each function takes torch tensors, checks that they are dense device tensors
+of the right dtype, and passes their device pointers, sizes and torch's
+current HIP stream to the C ABI declared in include/splitk.h.  Every step of
+the computation runs in the library's HIP kernels; nothing here computes.
+If the library has not been built, every call raises: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsplitk.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "splitk.h")
+
+DTYPE_CODE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+
+_STATUS_NAMES = {
+    0: "SPLITK_OK", 1: "SPLITK_ERR_NULL", 2: "SPLITK_ERR_DTYPE", 3: "SPLITK_ERR_SHAPE",
+    4: "SPLITK_ERR_SPLIT", 5: "SPLITK_ERR_ALIAS", 6: "SPLITK_ERR_ALIGN", 7: "SPLITK_ERR_RANGE",
+    8: "SPLITK_ERR_LAUNCH",
+}
+
+_lib = None
+
+
+class SplitKError(RuntimeError):
+    """A non-zero status from the library (nothing was launched)."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+def library_built() -> bool:
+    return os.path.exists(LIB_PATH)
+
+
+def load():
+    """Loads libsplitk.so once.  torch is imported first so that the library
+    binds to the HIP runtime torch already mapped (one runtime per process,
+    so torch's stream handles are valid in the library)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not library_built():
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with `python -m split_dense_gemm_amd.build` "
+            "(there is no fallback path)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.splitk_gemm_bt.argtypes = [P, P, P, I64, I64, I64, I64, I64, I, P]
+    lib.splitk_gemm_bt.restype = I
+    lib.splitk_reduce.argtypes = [P, P, I64, I64, I64, P]
+    lib.splitk_reduce.restype = I
+    lib.splitk_gemm_bt_reduce.argtypes = [P, P, P, P, I64, I64, I64, I64, I64, I, P]
+    lib.splitk_gemm_bt_reduce.restype = I
+    lib.splitk_status_str.argtypes = [I]
+    lib.splitk_status_str.restype = ctypes.c_char_p
+    lib.splitk_describe.argtypes = [I64, I64, I64, I64, I64, I, ctypes.c_char_p, I64]
+    lib.splitk_describe.restype = I
+    _lib = lib
+    return lib
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/splitk.h declares."""
+    text = open(HEADER_PATH).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(splitk_\w+)\s*\(", text, flags=re.M)
+
+
+def _check(status: int):
+    if status != 0:
+        msg = load().splitk_status_str(status).decode()
+        raise SplitKError(status, msg)
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dev(t: torch.Tensor, name: str):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _operands(A: torch.Tensor, B: torch.Tensor):
+    _dev(A, "A")
+    _dev(B, "B")
+    if A.dim() != 2 or B.dim() != 2:
+        raise ValueError("A must be [M,K] and B [N,K]")
+    if A.dtype != B.dtype or A.dtype not in DTYPE_CODE:
+        raise ValueError(f"A and B must share one of float32/float16/bfloat16, got {A.dtype}, {B.dtype}")
+    if A.shape[1] != B.shape[1]:
+        raise ValueError(f"A is {tuple(A.shape)} and B is {tuple(B.shape)}: K differs")
+    return A.shape[0], B.shape[0], A.shape[1], DTYPE_CODE[A.dtype]
+
+
+def _f32_out(t: torch.Tensor, name: str, numel: int):
+    _dev(t, name)
+    if t.dtype != torch.float32:
+        raise ValueError(f"{name} must be float32")
+    if t.numel() != numel:
+        raise ValueError(f"{name} must hold {numel} elements, got {t.numel()}")
+
+
+def gemm_bt(A: torch.Tensor, B: torch.Tensor, partials: torch.Tensor, k_per_split: int, splits: int,
+            stream=None) -> torch.Tensor:
+    """partials[s,i,j] = sum over split s's k range of A[i,k]*B[j,k] (see splitk.h)."""
+    M, N, K, dt = _operands(A, B)
+    _f32_out(partials, "partials", splits * M * N)
+    _check(load().splitk_gemm_bt(A.data_ptr(), B.data_ptr(), partials.data_ptr(), M, N, K,
+                                 int(k_per_split), int(splits), dt, _stream(stream)))
+    return partials
+
+
+def reduce(partials: torch.Tensor, C: torch.Tensor, splits: int, stream=None) -> torch.Tensor:
+    """C[i,j] = sum over s of partials[s,i,j] (see splitk.h)."""
+    if C.dim() != 2:
+        raise ValueError("C must be [M,N]")
+    M, N = C.shape
+    _f32_out(C, "C", M * N)
+    _f32_out(partials, "partials", splits * M * N)
+    _check(load().splitk_reduce(partials.data_ptr(), C.data_ptr(), int(splits), M, N, _stream(stream)))
+    return C
+
+
+def gemm_bt_reduce(A: torch.Tensor, B: torch.Tensor, partials: torch.Tensor, C: torch.Tensor,
+                   k_per_split: int, splits: int, stream=None) -> torch.Tensor:
+    """The split-K GEMM and the slab sum back to back on one stream (see splitk.h)."""
+    M, N, K, dt = _operands(A, B)
+    _f32_out(partials, "partials", splits * M * N)
+    _f32_out(C, "C", M * N)
+    _check(load().splitk_gemm_bt_reduce(A.data_ptr(), B.data_ptr(), partials.data_ptr(), C.data_ptr(),
+                                        M, N, K, int(k_per_split), int(splits), dt, _stream(stream)))
+    return C
+
+
+def describe(M: int, N: int, K: int, k_per_split: int, splits: int, dtype) -> str:
+    """The GEMM kernel configuration the library picks for this problem."""
+    code = DTYPE_CODE[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    buf = ctypes.create_string_buffer(128)
+    _check(load().splitk_describe(M, N, K, k_per_split, splits, code, buf, len(buf)))
+    return buf.value.decode()
+
+
+def raw_call(name: str, *args) -> int:
+    """Calls a C ABI entry point with raw integer arguments and returns its status
+    (used by the tests of the argument checks)."""
+    return int(getattr(load(), name)(*args))

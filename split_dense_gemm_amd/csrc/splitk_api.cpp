@@ -1,0 +1,148 @@
+// C ABI of the split-K GEMM library: argument checks, kernel choice, launch.
+//
+// The checks restate the launch contract of "Aligned shared rows for
+// pipelined NAX on CUDA" (section "Contract and correctness") and "Wider
+// consecutive-weight NAX GEMM" (section "Launch contract and correctness"):
+// M, K and k_per_split positive multiples of 32, N a positive multiple of 64,
+// every split starting below K with the splits covering K, exact extents and
+// outputs that alias nothing.  Each failed check returns its own status
+// before anything is enqueued; no HIP call is made until every check passed.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/splitk.h"
+#include "splitk_internal.h"
+
+namespace {
+
+constexpr int64_t kMaxElems = int64_t(1) << 31;  // 32-bit element indices in the kernels
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi) in bytes
+};
+
+bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int element_bytes(int dtype) { return dtype == SPLITK_F32 ? 4 : 2; }
+
+// Shape, split and size checks shared by the GEMM entry points.
+int check_gemm_shape(int64_t M, int64_t N, int64_t K, int64_t kps, int64_t splits, int dtype) {
+    if (dtype != SPLITK_F32 && dtype != SPLITK_F16 && dtype != SPLITK_BF16) return SPLITK_ERR_DTYPE;
+    if (M <= 0 || N <= 0 || K <= 0 || kps <= 0) return SPLITK_ERR_SHAPE;
+    if (M % 32 || K % 32 || kps % 32 || N % 64) return SPLITK_ERR_SHAPE;
+    if (M >= kMaxElems || N >= kMaxElems || K >= kMaxElems || kps >= kMaxElems) return SPLITK_ERR_RANGE;
+    // Every split starts below K and together they cover K.  With kps >= 32
+    // any valid split count is below K, so the products below cannot overflow.
+    if (splits < 1 || splits > K) return SPLITK_ERR_SPLIT;
+    if ((splits - 1) * kps >= K || splits * kps < K) return SPLITK_ERR_SPLIT;
+    if (M * K >= kMaxElems || N * K >= kMaxElems || M * N >= kMaxElems) return SPLITK_ERR_RANGE;
+    if (splits * (M * N) >= kMaxElems) return SPLITK_ERR_RANGE;
+    return SPLITK_OK;
+}
+
+// Pointer checks: alignment, then overlap of outputs with everything else.
+// C may be NULL (GEMM alone).
+int check_gemm_pointers(const void* A, const void* B, const float* P, const float* C, int64_t M,
+                        int64_t N, int64_t K, int64_t splits, int dtype) {
+    if (!aligned16(A) || !aligned16(B) || !aligned16(P) || (C && !aligned16(C))) return SPLITK_ERR_ALIGN;
+    const int64_t es = element_bytes(dtype);
+    const Range ra{(uintptr_t)A, (uintptr_t)A + (uintptr_t)(M * K * es)};
+    const Range rb{(uintptr_t)B, (uintptr_t)B + (uintptr_t)(N * K * es)};
+    const Range rp{(uintptr_t)P, (uintptr_t)P + (uintptr_t)(splits * M * N * 4)};
+    if (overlaps(rp, ra) || overlaps(rp, rb)) return SPLITK_ERR_ALIAS;
+    if (C) {
+        const Range rc{(uintptr_t)C, (uintptr_t)C + (uintptr_t)(M * N * 4)};
+        if (overlaps(rc, ra) || overlaps(rc, rb) || overlaps(rc, rp)) return SPLITK_ERR_ALIAS;
+    }
+    return SPLITK_OK;
+}
+
+int check_reduce(const float* P, const float* C, int64_t splits, int64_t M, int64_t N) {
+    if (!P || !C) return SPLITK_ERR_NULL;
+    if (M <= 0 || N <= 0 || M % 32 || N % 64) return SPLITK_ERR_SHAPE;
+    if (splits < 1) return SPLITK_ERR_SPLIT;
+    if (M >= kMaxElems || N >= kMaxElems || splits >= kMaxElems) return SPLITK_ERR_RANGE;
+    if (M * N >= kMaxElems || splits * (M * N) >= kMaxElems) return SPLITK_ERR_RANGE;
+    if (!aligned16(P) || !aligned16(C)) return SPLITK_ERR_ALIGN;
+    const Range rp{(uintptr_t)P, (uintptr_t)P + (uintptr_t)(splits * M * N * 4)};
+    const Range rc{(uintptr_t)C, (uintptr_t)C + (uintptr_t)(M * N * 4)};
+    if (overlaps(rp, rc)) return SPLITK_ERR_ALIAS;
+    return SPLITK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* splitk_status_str(int status) {
+    switch (status) {
+        case SPLITK_OK: return "ok";
+        case SPLITK_ERR_NULL: return "null pointer";
+        case SPLITK_ERR_DTYPE: return "unknown dtype";
+        case SPLITK_ERR_SHAPE:
+            return "bad shape: M, K and k_per_split must be positive multiples of 32, N a positive "
+                   "multiple of 64";
+        case SPLITK_ERR_SPLIT:
+            return "bad split geometry: every split must start below K and the splits must cover K";
+        case SPLITK_ERR_ALIAS: return "an output overlaps an input or the other output";
+        case SPLITK_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+        case SPLITK_ERR_RANGE: return "a buffer holds 2^31 elements or more";
+        case SPLITK_ERR_LAUNCH: return "kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+int splitk_gemm_bt(const void* A, const void* B, float* partials, int64_t M, int64_t N, int64_t K,
+                   int64_t k_per_split, int64_t splits, int dtype, void* stream) {
+    if (!A || !B || !partials) return SPLITK_ERR_NULL;
+    int st = check_gemm_shape(M, N, K, k_per_split, splits, dtype);
+    if (st != SPLITK_OK) return st;
+    st = check_gemm_pointers(A, B, partials, nullptr, M, N, K, splits, dtype);
+    if (st != SPLITK_OK) return st;
+    const splitk::GemmPlan plan = splitk::plan_gemm(dtype, M, N, K, k_per_split, splits);
+    hipError_t e = splitk::launch_gemm_bt(plan, A, B, partials, M, N, K, k_per_split, splits, dtype,
+                                          (hipStream_t)stream);
+    return e == hipSuccess ? SPLITK_OK : SPLITK_ERR_LAUNCH;
+}
+
+int splitk_reduce(const float* partials, float* C, int64_t splits, int64_t M, int64_t N, void* stream) {
+    int st = check_reduce(partials, C, splits, M, N);
+    if (st != SPLITK_OK) return st;
+    hipError_t e = splitk::launch_slab_reduce(partials, C, splits, M, N, (hipStream_t)stream);
+    return e == hipSuccess ? SPLITK_OK : SPLITK_ERR_LAUNCH;
+}
+
+int splitk_gemm_bt_reduce(const void* A, const void* B, float* partials, float* C, int64_t M,
+                          int64_t N, int64_t K, int64_t k_per_split, int64_t splits, int dtype,
+                          void* stream) {
+    if (!A || !B || !partials || !C) return SPLITK_ERR_NULL;
+    int st = check_gemm_shape(M, N, K, k_per_split, splits, dtype);
+    if (st != SPLITK_OK) return st;
+    st = check_gemm_pointers(A, B, partials, C, M, N, K, splits, dtype);
+    if (st != SPLITK_OK) return st;
+    const splitk::GemmPlan plan = splitk::plan_gemm(dtype, M, N, K, k_per_split, splits);
+    hipError_t e = splitk::launch_gemm_bt(plan, A, B, partials, M, N, K, k_per_split, splits, dtype,
+                                          (hipStream_t)stream);
+    if (e != hipSuccess) return SPLITK_ERR_LAUNCH;
+    e = splitk::launch_slab_reduce(partials, C, splits, M, N, (hipStream_t)stream);
+    return e == hipSuccess ? SPLITK_OK : SPLITK_ERR_LAUNCH;
+}
+
+int splitk_describe(int64_t M, int64_t N, int64_t K, int64_t k_per_split, int64_t splits, int dtype,
+                    char* buf, int64_t len) {
+    int st = check_gemm_shape(M, N, K, k_per_split, splits, dtype);
+    if (st != SPLITK_OK) return st;
+    const splitk::GemmPlan p = splitk::plan_gemm(dtype, M, N, K, k_per_split, splits);
+    if (buf && len > 0) {
+        static const char* const names[] = {"wavek"};
+        snprintf(buf, (size_t)len, "%s bm%d bn%d waves%d block%d grid%lld", names[p.kind], p.bm, p.bn,
+                 p.waves, p.block, (long long)p.grid);
+    }
+    return SPLITK_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,35 @@
+// Internal interface between the C ABI (splitk_api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace splitk {
+
+// Which GEMM kernel family serves a call.
+enum GemmKind : int {
+    // Every wave of a workgroup computes the whole BM x BN tile over its own
+    // share of the split's 128-byte k-chunks, loading MFMA fragments straight
+    // from global memory; the waves' accumulators are summed through LDS.
+    // Suited to the skinny, short shapes (M <= 256) where the grid is small.
+    kWaveK = 0,
+};
+
+struct GemmPlan {
+    int kind;
+    int bm, bn, waves;
+    int64_t grid;  // workgroups
+    int block;     // threads per workgroup
+};
+
+// Chooses the kernel configuration for a validated problem.
+GemmPlan plan_gemm(int dtype, int64_t M, int64_t N, int64_t K, int64_t kps, int64_t splits);
+
+hipError_t launch_gemm_bt(const GemmPlan& plan, const void* A, const void* B, float* partials,
+                          int64_t M, int64_t N, int64_t K, int64_t kps, int64_t splits, int dtype,
+                          hipStream_t stream);
+
+hipError_t launch_slab_reduce(const float* partials, float* C, int64_t splits, int64_t M, int64_t N,
+                              hipStream_t stream);
+
+}  // namespace splitk

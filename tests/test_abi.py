@@ -1,0 +1,133 @@
+"""Host-side tests of the C ABI: the library loads, exports what
+include/splitk.h declares, and rejects every argument the launch contract
+forbids ("Aligned shared rows for pipelined NAX on CUDA", section "Contract
+and correctness") before launching anything.
+
+No test here launches a kernel.  The pointer checks pass made-up addresses,
+which the library must reject before any HIP call; they are skipped where a
+GPU is present, and the GPU tests cover the same statuses with real buffers.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import pytest
+
+from conftest import gpu_available
+from split_dense_gemm_amd import inputs
+
+OK, NULL, DTYPE, SHAPE, SPLIT, ALIAS, ALIGN, RANGE = 0, 1, 2, 3, 4, 5, 6, 7
+
+BF16 = inputs.DTYPE_CODES["bf16"]
+
+
+def test_exports_every_declared_symbol(hip_lib):
+    names = hip_lib.header_functions()
+    assert set(names) == {"splitk_gemm_bt", "splitk_reduce", "splitk_gemm_bt_reduce",
+                          "splitk_status_str", "splitk_describe"}
+    lib = hip_lib.load()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(hip_lib):
+    lib = hip_lib.load()
+    texts = [lib.splitk_status_str(s).decode() for s in range(9)]
+    assert texts[0] == "ok" and len(set(texts)) == 9
+    assert lib.splitk_status_str(99).decode() == "unknown status"
+
+
+# (M, N, K, kps, splits, dtype) -> status from the shape and split checks
+SHAPE_CASES = [
+    ((256, 1024, 2048, 1024, 2, BF16), OK),
+    ((32, 64, 64, 32, 2, 0), OK),
+    ((32, 512, 2080, 544, 4, 1), OK),
+    ((64, 128, 1056, 1024, 2, BF16), OK),     # last split of 32
+    ((256, 1024, 2048, 1024, 2, 3), DTYPE),
+    ((256, 1024, 2048, 1024, 2, -1), DTYPE),
+    ((0, 64, 64, 32, 2, BF16), SHAPE),
+    ((48, 64, 64, 32, 2, BF16), SHAPE),       # M not a multiple of 32
+    ((32, 96, 64, 32, 2, BF16), SHAPE),       # N not a multiple of 64
+    ((32, 32, 64, 32, 2, BF16), SHAPE),
+    ((32, 64, 48, 48, 1, BF16), SHAPE),       # K not a multiple of 32
+    ((32, 64, 64, 16, 4, BF16), SHAPE),       # kps not a multiple of 32
+    ((32, 64, -64, 32, 2, BF16), SHAPE),
+    ((32, 64, 2048, 512, 0, BF16), SPLIT),
+    ((32, 64, 2048, 512, 3, BF16), SPLIT),    # splits do not cover K
+    ((32, 64, 2048, 512, 5, BF16), SPLIT),    # fifth split would start at K
+    ((32, 64, 2048, 4096, 2, BF16), SPLIT),   # second split would start past K
+    ((32, 64, 2080, 544, 3, BF16), SPLIT),
+    ((32, 64, 2**31, 2**31, 1, BF16), RANGE),
+    ((2**20, 64, 2**12, 2**12, 1, BF16), RANGE),  # M*K = 2^32 elements
+    ((2**16, 2**16, 32, 32, 1, BF16), RANGE),      # M*N = 2^32
+    ((2**15, 2**15, 64, 32, 2, BF16), RANGE),      # splits*M*N = 2^31
+]
+
+
+@pytest.mark.parametrize("args,status", SHAPE_CASES)
+def test_describe_checks_shape_and_split(hip_lib, args, status):
+    buf = ctypes.create_string_buffer(128)
+    got = hip_lib.load().splitk_describe(*args, buf, len(buf))
+    assert got == status
+    if status == OK:
+        assert buf.value.startswith(b"wavek")
+
+
+def test_plan_for_each_workload(hip_lib):
+    for w in inputs.WORKLOADS.values():
+        text = hip_lib.describe(w.M, w.N, w.K, w.kps, w.splits, inputs.DTYPE_CODES[w.dtype])
+        assert "grid" in text
+
+
+A_PTR, B_PTR, P_PTR, C_PTR = 0x10000000, 0x20000000, 0x30000000, 0x40000000
+
+
+@pytest.mark.skipif(gpu_available(), reason="made-up pointers are only passed where no GPU exists")
+class TestPointerChecksWithoutDevice:
+    def gemm(self, hip_lib, A=A_PTR, B=B_PTR, P=P_PTR, M=256, N=1024, K=2048, kps=1024, S=2, dt=BF16):
+        return hip_lib.raw_call("splitk_gemm_bt", A, B, P, M, N, K, kps, S, dt, None)
+
+    def fused(self, hip_lib, A=A_PTR, B=B_PTR, P=P_PTR, C=C_PTR, M=256, N=1024, K=2048, kps=1024,
+              S=2, dt=BF16):
+        return hip_lib.raw_call("splitk_gemm_bt_reduce", A, B, P, C, M, N, K, kps, S, dt, None)
+
+    def test_null(self, hip_lib):
+        assert self.gemm(hip_lib, A=None) == NULL
+        assert self.gemm(hip_lib, B=None) == NULL
+        assert self.gemm(hip_lib, P=None) == NULL
+        assert self.fused(hip_lib, C=None) == NULL
+        assert hip_lib.raw_call("splitk_reduce", None, C_PTR, 2, 256, 1024, None) == NULL
+        assert hip_lib.raw_call("splitk_reduce", P_PTR, None, 2, 256, 1024, None) == NULL
+
+    def test_alignment(self, hip_lib):
+        assert self.gemm(hip_lib, A=A_PTR + 8) == ALIGN
+        assert self.gemm(hip_lib, B=B_PTR + 2) == ALIGN
+        assert self.gemm(hip_lib, P=P_PTR + 4) == ALIGN
+        assert self.fused(hip_lib, C=C_PTR + 4) == ALIGN
+        assert hip_lib.raw_call("splitk_reduce", P_PTR + 4, C_PTR, 2, 256, 1024, None) == ALIGN
+
+    def test_aliasing(self, hip_lib):
+        a_bytes = 256 * 2048 * 2
+        assert self.gemm(hip_lib, P=A_PTR) == ALIAS
+        assert self.gemm(hip_lib, P=A_PTR + a_bytes - 16) == ALIAS        # tail overlap
+        assert self.gemm(hip_lib, P=B_PTR - 16) == ALIAS                   # head overlap
+        p_bytes = 2 * 256 * 1024 * 4
+        assert self.fused(hip_lib, C=P_PTR + p_bytes - 16) == ALIAS
+        assert self.fused(hip_lib, C=A_PTR) == ALIAS
+        assert hip_lib.raw_call("splitk_reduce", P_PTR, P_PTR + 1024, 2, 256, 1024, None) == ALIAS
+
+    def test_shape_errors_come_before_pointer_checks(self, hip_lib):
+        assert self.gemm(hip_lib, A=A_PTR + 8, M=48) == SHAPE
+        assert self.gemm(hip_lib, P=A_PTR, S=3) == SPLIT
+        assert hip_lib.raw_call("splitk_reduce", P_PTR, C_PTR, 0, 256, 1024, None) == SPLIT
+        assert hip_lib.raw_call("splitk_reduce", P_PTR, C_PTR, 2, 256, 96, None) == SHAPE
+
+
+def test_binding_rejects_host_tensors(hip_lib):
+    import torch
+
+    a = torch.zeros(32, 64, dtype=torch.bfloat16)
+    b = torch.zeros(64, 64, dtype=torch.bfloat16)
+    p = torch.zeros(2, 32, 64)
+    with pytest.raises(ValueError):
+        hip_lib.gemm_bt(a, b, p, 32, 2)

@@ -1,0 +1,318 @@
+"""GPU parity: the HIP kernels, called through the C ABI, against the
+binary64 reference (oracle/).
+
+Acceptance follows the pages ("Aligned shared rows for pipelined NAX on
+CUDA", section "Contract and correctness"; "Wider consecutive-weight NAX
+GEMM", sections "Launch contract and correctness" and "Performance
+method"): every partial within 1e-4 and the final output within 1e-4 (F32
+inputs), 2e-3 (F16) or 2e-2 (BF16), the error being |gpu - ref| divided by
+the sum of |products| behind the reference value (exact zero required where
+that sum is zero); outputs poisoned before the call (7.0, and separately a
+quiet NaN so that any element left unwritten fails); 64 trailing guard
+elements at 11.0 that must come back bit-for-bit.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from split_dense_gemm_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+PARTIAL_TOL = 1e-4
+FINAL_TOL = {"f32": 1e-4, "f16": 2e-3, "bf16": 2e-2}
+GUARD_BITS = np.float32(inputs.GUARD_VALUE).view(np.uint32)
+
+
+@pytest.fixture(scope="module")
+def sdg(hip_lib):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return hip_lib
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _vals(t):
+    return oracle.decode(inputs.stored_bits(t), inputs.dtype_name(t))
+
+
+class Run:
+    """One GEMM + slab sum on the GPU with guarded, poisoned outputs."""
+
+    def __init__(self, sdg, a, b, kps, S, poison="seven", separate=False, stream=None):
+        dev = torch.device("cuda:0")
+        self.M, self.K = a.shape
+        self.N = b.shape[0]
+        self.S = S
+        n_p, n_c = S * self.M * self.N, self.M * self.N
+        self.pbuf = inputs.guarded_buffer(n_p, poison).to(dev)
+        self.cbuf = inputs.guarded_buffer(n_c, poison).to(dev)
+        P = self.pbuf[:n_p].view(S, self.M, self.N)
+        C = self.cbuf[:n_c].view(self.M, self.N)
+        ad, bd = a.to(dev), b.to(dev)
+        if separate:
+            sdg.gemm_bt(ad, bd, P, kps, S, stream=stream)
+            sdg.reduce(P, C, S, stream=stream)
+        else:
+            sdg.gemm_bt_reduce(ad, bd, P, C, kps, S, stream=stream)
+        torch.cuda.synchronize()
+        self.p_all = self.pbuf.cpu().numpy()
+        self.c_all = self.cbuf.cpu().numpy()
+        self.P = self.p_all[:n_p].reshape(S, self.M, self.N)
+        self.C = self.c_all[:n_c].reshape(self.M, self.N)
+
+    def guards_intact(self):
+        return (np.all(self.p_all[-inputs.GUARD_COUNT:].view(np.uint32) == GUARD_BITS) and
+                np.all(self.c_all[-inputs.GUARD_COUNT:].view(np.uint32) == GUARD_BITS))
+
+
+def check_against_oracle(sdg, a, b, kps, S, dtype, poison="seven", separate=False):
+    a64, b64 = _vals(a), _vals(b)
+    RP, DP, _ = oracle.splitk_partials(a64, b64, kps, S)
+    RC, DC, _ = oracle.gemm_bt(a64, b64)
+    run = Run(sdg, a, b, kps, S, poison=poison, separate=separate)
+    ep, ip = oracle.normalized_error(run.P, RP, DP)
+    ec, ic = oracle.normalized_error(run.C, RC, DC)
+    _say(f"  partial err {ep:.3e} at {np.unravel_index(max(ip, 0), RP.shape)}, "
+         f"final err {ec:.3e} at {np.unravel_index(max(ic, 0), RC.shape)}")
+    assert run.guards_intact(), "a trailing guard changed"
+    assert ep <= PARTIAL_TOL, f"partial error {ep}"
+    assert ec <= FINAL_TOL[dtype], f"final error {ec}"
+    return run, (RP, DP, RC, DC)
+
+
+# The measured workloads except the largest (checked by sampling below).
+SMALL_WORKLOADS = [n for n, w in inputs.WORKLOADS.items() if w.M * w.N * w.K <= 2**31]
+
+
+@pytest.mark.parametrize("name", SMALL_WORKLOADS)
+@pytest.mark.parametrize("poison", ["seven", "nan"])
+def test_workload_full_parity(sdg, name, poison):
+    w = inputs.WORKLOADS[name]
+    _say(f"case {name} poison={poison}")
+    a, b = inputs.workload_operands(w)
+    run, _ = check_against_oracle(sdg, a, b, w.kps, w.splits, w.dtype, poison=poison)
+    if w.zero_first_row:
+        assert np.all(run.P[:, 0, :] == 0) and np.all(run.C[0] == 0)
+
+
+# Ten shapes x three dtypes: a single tile, non-square, a short final split,
+# odd tile counts, long K, skinny, larger, and the measured shapes.
+TEN_SHAPES = [
+    (32, 64, 32, 32, 1),
+    (64, 192, 256, 128, 2),
+    (32, 512, 2080, 544, 4),
+    (96, 320, 480, 160, 3),
+    (32, 64, 8192, 2048, 4),
+    (32, 512, 2048, 512, 4),
+    (512, 1024, 1024, 512, 2),
+    (96, 512, 2048, 512, 4),
+    (256, 512, 2048, 1024, 2),
+    (256, 1024, 2048, 1024, 2),
+]
+EXTRA_SHAPES = [
+    (64, 128, 1056, 1024, 2),   # final split of 32
+    (96, 512, 512, 128, 4),     # short K
+    (64, 128, 2048, 32, 64),    # 64 splits of 32
+    (160, 192, 608, 96, 7),     # five row blocks, seven splits, final split 32
+    (32, 64, 64, 64, 1),        # one split
+]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("shape", TEN_SHAPES + EXTRA_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_shape_sweep(sdg, shape, dtype):
+    M, N, K, kps, S = shape
+    _say(f"case {dtype} M{M} N{N} K{K} kps{kps} S{S}")
+    a, b = inputs.make_operands(M, N, K, dtype, seed=M * 7 + N * 3 + K + S, zero_first_row=True,
+                                scale_last_row=True)
+    run, _ = check_against_oracle(sdg, a, b, kps, S, dtype)
+    assert np.all(run.P[:, 0, :] == 0) and np.all(run.C[0] == 0)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("shape", [(32, 64, 64, 32, 2), (96, 320, 480, 160, 3),
+                                   (32, 512, 2080, 544, 4), (256, 1024, 2048, 1024, 2)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_exact_inputs_bitwise(sdg, shape, dtype):
+    """Entries j/8 make every F32 sum exact in any order: partials and C must
+    equal the reference bit for bit."""
+    M, N, K, kps, S = shape
+    _say(f"case exact {dtype} M{M} N{N} K{K} kps{kps} S{S}")
+    a, b = inputs.exact_operands(M, N, K, dtype, seed=5 + S)
+    a64, b64 = _vals(a), _vals(b)
+    RP, _, _ = oracle.splitk_partials(a64, b64, kps, S)
+    RC, _, _ = oracle.gemm_bt(a64, b64)
+    run = Run(sdg, a, b, kps, S, poison="nan")
+    assert run.guards_intact()
+    np.testing.assert_array_equal(run.P.astype(np.float64), RP)
+    np.testing.assert_array_equal(run.C.astype(np.float64), RC)
+
+
+def test_closed_forms_on_gpu(sdg):
+    """All-ones operands give each split's length (pins the last-split cut);
+    a one-hot A gives C = B^T on the leading block (pins orientation)."""
+    M, N, K, kps, S = 32, 512, 2080, 544, 4
+    a = torch.ones(M, K, dtype=torch.float16)
+    b = torch.ones(N, K, dtype=torch.float16)
+    run = Run(sdg, a, b, kps, S, poison="nan")
+    for s, length in enumerate([544, 544, 544, 448]):
+        assert np.all(run.P[s] == length)
+    assert np.all(run.C == K)
+    M, N, K = 64, 128, 256
+    a = torch.eye(M, K, dtype=torch.bfloat16)
+    _, b = inputs.make_operands(M, N, K, "bf16", seed=3)
+    run = Run(sdg, a, b, 128, 2, poison="nan")
+    want = b[:, :M].to(torch.float32).T.numpy()
+    np.testing.assert_array_equal(run.C, want)
+    np.testing.assert_array_equal(run.P[0], want)
+    assert np.all(run.P[1] == 0)
+
+
+def test_row_scaled_by_four_is_exactly_four_times(sdg):
+    M, N, K, kps, S = 64, 256, 1024, 512, 2
+    a, b = inputs.make_operands(M, N, K, "bf16", seed=8)
+    a[5] = a[9] * 4
+    run = Run(sdg, a, b, kps, S)
+    np.testing.assert_array_equal(run.P[:, 5, :], 4 * run.P[:, 9, :])
+    np.testing.assert_array_equal(run.C[5], 4 * run.C[9])
+
+
+def test_repeated_calls_are_bitwise_identical(sdg):
+    w = inputs.WORKLOADS[inputs.HEADLINE]
+    a, b = inputs.workload_operands(w)
+    r1 = Run(sdg, a, b, w.kps, w.splits)
+    r2 = Run(sdg, a, b, w.kps, w.splits, poison="nan")
+    assert np.array_equal(r1.P.view(np.uint32), r2.P.view(np.uint32))
+    assert np.array_equal(r1.C.view(np.uint32), r2.C.view(np.uint32))
+
+
+def test_separate_calls_match_fused_call(sdg):
+    w = inputs.WORKLOADS["f16_m32_n512_k2080_s4"]
+    a, b = inputs.workload_operands(w)
+    r1 = Run(sdg, a, b, w.kps, w.splits)
+    r2 = Run(sdg, a, b, w.kps, w.splits, separate=True)
+    assert np.array_equal(r1.P.view(np.uint32), r2.P.view(np.uint32))
+    assert np.array_equal(r1.C.view(np.uint32), r2.C.view(np.uint32))
+
+
+def test_runs_on_a_side_stream(sdg):
+    w = inputs.WORKLOADS["bf16_m96_n512_k2048_s4"]
+    a, b = inputs.workload_operands(w)
+    ref = Run(sdg, a, b, w.kps, w.splits)
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        got = Run(sdg, a, b, w.kps, w.splits, poison="nan", stream=side)
+    assert np.array_equal(ref.C.view(np.uint32), got.C.view(np.uint32))
+
+
+def test_graph_replays_match_eager(sdg):
+    """The chain captured into a HIP graph and replayed several times, with
+    eager work and synchronisation in between; every replay must match."""
+    w = inputs.WORKLOADS[inputs.HEADLINE]
+    a, b = inputs.workload_operands(w)
+    eager = Run(sdg, a, b, w.kps, w.splits)
+    dev = torch.device("cuda:0")
+    ad, bd = a.to(dev), b.to(dev)
+    P = torch.empty(w.splits, w.M, w.N, device=dev)
+    C = torch.empty(w.M, w.N, device=dev)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        sdg.gemm_bt_reduce(ad, bd, P, C, w.kps, w.splits)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(3):
+            sdg.gemm_bt_reduce(ad, bd, P, C, w.kps, w.splits)
+    for rep in range(4):
+        P.fill_(float("nan"))
+        C.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(C.cpu().numpy().view(np.uint32), eager.C.view(np.uint32)), rep
+        assert np.array_equal(P.cpu().numpy().view(np.uint32), eager.P.view(np.uint32)), rep
+
+
+def test_largest_workload_sampled(sdg):
+    """The 2048x4096x4096, 8-split workload in the configuration the
+    benchmark times: 4096 sampled outputs against the reference one by one,
+    plus properties checked everywhere (no element left at the NaN poison,
+    guards intact, sum of slabs close to C)."""
+    w = inputs.WORKLOADS["bf16_m2048_n4096_k4096_s8"]
+    _say(f"case {w.name} (sampled)")
+    a, b = inputs.workload_operands(w)
+    run = Run(sdg, a, b, w.kps, w.splits, poison="nan")
+    assert run.guards_intact()
+    assert not np.isnan(run.P).any() and not np.isnan(run.C).any()
+    rng = np.random.default_rng(11)
+    rows = np.concatenate([rng.integers(0, w.M, 4090), [0, w.M - 1, 0, w.M - 1, 1023, 1024]])
+    cols = np.concatenate([rng.integers(0, w.N, 4090), [0, w.N - 1, w.N - 1, 0, 2047, 2048]])
+    a64, b64 = _vals(a), _vals(b)
+    SP, SDP, SC, SDC = oracle.sampled(a64, b64, w.kps, w.splits, rows, cols)
+    gp = run.P[:, rows, cols].T
+    gc = run.C[rows, cols]
+    ep, _ = oracle.normalized_error(gp, SP, SDP)
+    ec, _ = oracle.normalized_error(gc, SC, SDC)
+    _say(f"  sampled partial err {ep:.3e}, final err {ec:.3e}")
+    assert ep <= PARTIAL_TOL and ec <= FINAL_TOL["bf16"]
+    # Everywhere: C equals the F32 sum of the slabs up to the reduction's rounding.
+    s64 = run.P.astype(np.float64).sum(axis=0)
+    mag = np.abs(run.P.astype(np.float64)).sum(axis=0)
+    assert np.all(np.abs(run.C - s64) <= w.splits * 2.0**-24 * mag)
+
+
+@pytest.mark.parametrize("S", [1, 2, 3, 4, 5, 8, 13])
+def test_reduce_alone(sdg, S):
+    """The slab sum alone on random F32 slabs: within the F32 rounding of an
+    S-term sum, (S-1) * 2^-24 of the sum of |values|; bit-exact on values
+    whose sums are exact."""
+    M, N = 96, 320
+    dev = torch.device("cuda:0")
+    gen = torch.Generator().manual_seed(S)
+    slabs = torch.randn(S, M, N, generator=gen) * 3
+    cbuf = inputs.guarded_buffer(M * N, "nan").to(dev)
+    sdg.reduce(slabs.to(dev), cbuf[: M * N].view(M, N), S)
+    torch.cuda.synchronize()
+    got = cbuf.cpu().numpy()
+    ref, D, _ = oracle.slab_sum(slabs.numpy())
+    err, _ = oracle.normalized_error(got[: M * N], ref, D)
+    assert err <= max(S - 1, 0) * 2.0**-24 * 1.0001
+    assert np.all(got[M * N:].view(np.uint32) == GUARD_BITS)
+    ints = torch.randint(-1000, 1000, (S, M, N), generator=gen).float()
+    C = torch.empty(M, N, device=dev)
+    sdg.reduce(ints.to(dev), C, S)
+    ref, _, _ = oracle.slab_sum(ints.numpy())
+    np.testing.assert_array_equal(C.cpu().numpy().astype(np.float64), ref)
+
+
+def test_error_statuses_with_real_buffers(sdg):
+    """Misaligned pointers and overlapping outputs are rejected (nothing is
+    launched), with real device memory behind every pointer."""
+    dev = torch.device("cuda:0")
+    M, N, K, kps, S = 64, 128, 256, 128, 2
+    pool = torch.zeros(1 << 20, dtype=torch.float32, device=dev)  # 4 MiB
+    base = pool.data_ptr()
+    A, B, P, C = base, base + (1 << 16), base + (1 << 17), base + (1 << 19)
+    call = lambda *a: sdg.raw_call("splitk_gemm_bt_reduce", *a)  # noqa: E731
+    bf = inputs.DTYPE_CODES["bf16"]
+    assert call(A + 4, B, P, C, M, N, K, kps, S, bf, None) == 6
+    assert call(A, B, P + 8, C, M, N, K, kps, S, bf, None) == 6
+    assert call(A, B, A, C, M, N, K, kps, S, bf, None) == 5
+    assert call(A, B, P, P + 4096, M, N, K, kps, S, bf, None) == 5
+    assert sdg.raw_call("splitk_reduce", P, P + 1024, S, M, N, None) == 5
+    assert sdg.raw_call("splitk_gemm_bt", A, B, B, M, N, K, kps, S, bf, None) == 5
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(pool).item() == 0  # nothing ran
+    with pytest.raises(sdg.SplitKError):
+        a = torch.zeros(M, K, dtype=torch.bfloat16, device=dev)
+        b = torch.zeros(N, K, dtype=torch.bfloat16, device=dev)
+        sdg.gemm_bt(a, b, torch.zeros(3, M, N, device=dev), kps, 3)

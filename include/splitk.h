@@ -112,7 +112,7 @@ const char* splitk_status_str(int status);
 /*
  * Describes, without launching anything, the GEMM kernel configuration the
  * library would use for these arguments: writes a NUL-terminated text such as
- * "wavek bm32 bn64 waves4 grid256" into buf (at most `len` bytes, truncated).
+ * "wavek bm32 bn64 waves4 stages4 block256 grid256" into buf (at most `len` bytes, truncated).
  * Returns a splitk_status from the same argument checks as splitk_gemm_bt,
  * minus the pointer checks.
  */

@@ -34,6 +34,9 @@
 //    it from that XCD's L2.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include "splitk_internal.h"
 
@@ -46,9 +49,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kChunkBytes = 128;  // one chunk: 128 bytes of a row
-constexpr int kHalfBytes = 64;    // the part of a chunk one lane reads
-constexpr int kPieces = 4;        // 16-byte loads per lane per chunk and block
+constexpr int kChunkBytes = 128;  // one chunk: 128 bytes of a row (8 pieces of 16 bytes)
 
 // Element-type specific MFMA step on one 16-byte piece of each operand.
 template <int DT>
@@ -96,7 +97,14 @@ __device__ inline int xcd_logical_id(int b, int n) {
     return x < r ? x * (q + 1) + slot : r * (q + 1) + (x - r) * q + slot;
 }
 
-template <int DT, int BM, int BN, int W>
+// LDS slot of 16-byte piece p of staged row r.  XOR-swizzled so that the
+// fragment reads below (32 rows, one piece each) are conflict-free whether
+// the LDS serves 8 or 16 lanes of a 16-byte read per cycle: over any 16
+// consecutive rows, rows of equal parity get 8 distinct slots, and over any 8
+// consecutive rows all slots differ.
+__device__ inline int slot_of(int r, int p) { return p ^ (r & 7) ^ ((r >> 3) & 1); }
+
+template <int DT, int BM, int BN, int W, int D>
 __global__ __launch_bounds__(W * 64) void gemm_bt_wavek(const uint8_t* __restrict__ A,
                                                         const uint8_t* __restrict__ B,
                                                         float* __restrict__ P, int M, int N, int K,
@@ -105,8 +113,16 @@ __global__ __launch_bounds__(W * 64) void gemm_bt_wavek(const uint8_t* __restric
     constexpr int ES = Op::kElemBytes;
     constexpr int CK = kChunkBytes / ES;  // elements per chunk
     constexpr int MB = BM / 32, NB = BN / 32;
-    constexpr int PITCH = BN + 8;  // floats per row of the LDS reduction tile
-    __shared__ float red[W][BM][PITCH];
+    constexpr int ROWS = BM + BN;         // staged rows per chunk: A rows, then B rows
+    constexpr int LOADS = ROWS / 8;       // 16-byte loads per lane per chunk
+    constexpr int PITCH = BN + 8;         // floats per row of the LDS reduction tile
+    static_assert(ROWS % 8 == 0, "tile rows");
+    // One LDS block: per-wave staging buffers during the k loop, then (after
+    // a barrier) the W partial tiles of the cross-wave sum.
+    constexpr int STAGE_BYTES = W * ROWS * kChunkBytes;
+    constexpr int RED_BYTES = W * BM * PITCH * 4;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[STAGE_BYTES > RED_BYTES ? STAGE_BYTES : RED_BYTES];
+    float (*red)[BM][PITCH] = reinterpret_cast<float (*)[BM][PITCH]>(smem);
 
     const int logical = xcd_logical_id(blockIdx.x, gridDim.x);
     const int mt = logical % tiles_m;
@@ -122,16 +138,25 @@ __global__ __launch_bounds__(W * 64) void gemm_bt_wavek(const uint8_t* __restric
     const int k0 = s * kps;
     const int k1 = min(k0 + kps, K);
     const int nchunks = (k1 - k0 + CK - 1) / CK;
+    // This wave owns chunks wave, wave + W, wave + 2W, ... (wave-uniform count).
+    const int mine = wave < nchunks ? (nchunks - wave + W - 1) / W : 0;
 
+    // Coalesced loads: load i of a lane covers staged row 8*i + lane/8 and
+    // writes LDS slot lane%8 of it, so each load instruction of the wave reads
+    // eight whole 128-byte row segments and writes 1 KiB of LDS contiguously.
     const size_t row_bytes = (size_t)K * ES;
-    const uint8_t* a_row[MB];
-    const uint8_t* b_row[NB];
+    const int lrow = lane >> 3, lslot = lane & 7;
+    const uint8_t* src[LOADS];
+    int piece[LOADS];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-        a_row[mb] = A + (size_t)(mt * BM + mb * 32 + r) * row_bytes + (size_t)k0 * ES + h * kHalfBytes;
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-        b_row[nb] = B + (size_t)(nt * BN + nb * 32 + r) * row_bytes + (size_t)k0 * ES + h * kHalfBytes;
+    for (int i = 0; i < LOADS; ++i) {
+        const int row = 8 * i + lrow;
+        src[i] = row < BM ? A + (size_t)(mt * BM + row) * row_bytes
+                          : B + (size_t)(nt * BN + row - BM) * row_bytes;
+        src[i] += (size_t)k0 * ES;
+        piece[i] = slot_of(row, lslot);  // the global piece that lands in slot lslot
+    }
+    uint8_t* lds = smem + wave * ROWS * kChunkBytes;
 
     f32x16 acc[MB][NB];
 #pragma unroll
@@ -139,46 +164,74 @@ __global__ __launch_bounds__(W * 64) void gemm_bt_wavek(const uint8_t* __restric
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x16{};
 
-    u32x4 av[MB][kPieces], bv[NB][kPieces];
-    auto load = [&](int c) {
-        // This lane's half of chunk c holds elements starting at k0 + c*CK + h*CK/2.
-        const bool valid = c < nchunks && (k0 + c * CK + h * (CK / 2)) < k1;
+    u32x4 stg[D][LOADS];
+
+    // Chunk id of this wave's t-th chunk, clamped into range so that every
+    // global load is unconditional (a clamped load re-reads a real chunk and
+    // is never consumed).  Straight-line loads let the compiler wait for
+    // exactly the stage it is about to use while later stages stay in flight.
+    auto chunk_of = [&](int t) { return mine > 0 ? wave + min(t, mine - 1) * W : 0; };
+    // The upper half of a chunk (pieces 4..7) lies past the slice end only in
+    // the last chunk of a 16-bit slice whose length is an odd multiple of 32.
+    auto half_chunk = [&](int c) { return k0 + c * CK + CK / 2 >= k1; };
+
+    auto load = [&](int c, u32x4 (&t)[LOADS]) {
+        // In a half chunk the lanes meant for pieces 4..7 re-read pieces 0..3
+        // (in bounds); those slots are never consumed.
+        const int mask = half_chunk(c) ? 3 : 7;
         const size_t off = (size_t)c * kChunkBytes;
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-            for (int q = 0; q < kPieces; ++q)
-                av[mb][q] = valid ? *(const u32x4*)(a_row[mb] + off + q * 16) : u32x4{};
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-            for (int q = 0; q < kPieces; ++q)
-                bv[nb][q] = valid ? *(const u32x4*)(b_row[nb] + off + q * 16) : u32x4{};
+        for (int i = 0; i < LOADS; ++i) t[i] = *(const u32x4*)(src[i] + off + (piece[i] & mask) * 16);
     };
-
-    if (wave < nchunks) load(wave);
-    for (int c = wave; c < nchunks; c += W) {
-        u32x4 ca[MB][kPieces], cb[NB][kPieces];
+    auto compute = [&](int c, u32x4 (&t)[LOADS]) {
+        // Stage the chunk in this wave's LDS buffer (row 8*i + lane/8, slot lane%8).
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
+        for (int i = 0; i < LOADS; ++i) *(u32x4*)(lds + i * 1024 + lane * 16) = t[i];
+        // MFMA step q takes pieces 2q (lanes 0-31) and 2q+1 (lanes 32-63) of
+        // each of the 32 rows of a block: 16 consecutive k for both operands.
+        const int steps = half_chunk(c) ? 2 : 4;
 #pragma unroll
-            for (int q = 0; q < kPieces; ++q) ca[mb][q] = av[mb][q];
+        for (int q = 0; q < 4; ++q) {
+            if (q >= steps) break;
+            u32x4 fa[MB], fb[NB];
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
+            for (int mb = 0; mb < MB; ++mb) {
+                const int row = mb * 32 + r;
+                fa[mb] = *(const u32x4*)(lds + row * kChunkBytes + slot_of(row, 2 * q + h) * 16);
+            }
 #pragma unroll
-            for (int q = 0; q < kPieces; ++q) cb[nb][q] = bv[nb][q];
-        if (c + W < nchunks) load(c + W);  // prefetch the next chunk of this wave
-#pragma unroll
-        for (int q = 0; q < kPieces; ++q)
+            for (int nb = 0; nb < NB; ++nb) {
+                const int row = BM + nb * 32 + r;
+                fb[nb] = *(const u32x4*)(lds + row * kChunkBytes + slot_of(row, 2 * q + h) * 16);
+            }
 #pragma unroll
             for (int e = 0; e < Op::kStepsPerPiece; ++e)
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
                     for (int nb = 0; nb < NB; ++nb)
-                        acc[mb][nb] = Op::step(ca[mb][q], cb[nb][q], acc[mb][nb], e);
-    }
+                        acc[mb][nb] = Op::step(fa[mb], fb[nb], acc[mb][nb], e);
+        }
+    };
 
+    // Prologue: D chunks in flight before the first MFMA.
+#pragma unroll
+    for (int j = 0; j < D; ++j) load(chunk_of(j), stg[j]);
+    // Steady state: consume stage j, then refill it with the chunk D ahead.
+    int t = 0;
+    for (; t + D < mine; t += D) {
+#pragma unroll
+        for (int j = 0; j < D; ++j) {
+            compute(chunk_of(t + j), stg[j]);
+            load(chunk_of(t + j + D), stg[j]);
+        }
+    }
+    // Epilogue: the stages still holding real chunks (no loads issued here).
+#pragma unroll
+    for (int j = 0; j < D; ++j)
+        if (t + j < mine) compute(chunk_of(t + j), stg[j]);
+
+    __syncthreads();  // every wave is done with its staging buffer
     // 32x32 accumulator layout: register i of lane l holds
     // row 8*(i/4) + 4*(l/32) + i%4, column l%32 of the block.
 #pragma unroll
@@ -203,7 +256,164 @@ __global__ __launch_bounds__(W * 64) void gemm_bt_wavek(const uint8_t* __restric
     }
 }
 
-template <int DT, int BM, int BN, int W>
+// Large-tile kernel: each workgroup owns a BM x BN output tile of one split
+// and its WM x WN waves share every staged chunk.  Per 128-byte k-chunk the
+// whole workgroup loads BM + BN rows with coalesced 16-byte loads (eight
+// complete row segments per instruction), writes them to one of two swizzled
+// LDS buffers, and after one barrier every wave reads the fragments of its
+// (BM/WM) x (BN/WN) sub-tile while the next chunk's global loads are in
+// flight.  Accumulators are stored straight to the partial slab: for each
+// accumulator register the 32 lanes of a half-wave write 32 consecutive
+// floats of one row.
+template <int DT, int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_bt_tiled(const uint8_t* __restrict__ A,
+                                                              const uint8_t* __restrict__ B,
+                                                              float* __restrict__ P, int M, int N,
+                                                              int K, int kps, int tiles_m,
+                                                              int tiles_n) {
+    using Op = Mfma<DT>;
+    constexpr int ES = Op::kElemBytes;
+    constexpr int CK = kChunkBytes / ES;
+    constexpr int NT = WM * WN * 64;          // threads
+    constexpr int ROWS = BM + BN;             // staged rows per chunk
+    constexpr int LOADS = ROWS * 8 / NT;      // 16-byte loads per thread per chunk
+    constexpr int TM = BM / WM, TN = BN / WN; // per-wave sub-tile
+    constexpr int MB = TM / 32, NB = TN / 32;
+    constexpr int GM = 4;                     // row tiles per group of the tile order
+    static_assert(ROWS * 8 % NT == 0, "staging split");
+    __shared__ __attribute__((aligned(16))) uint8_t smem[2][ROWS * kChunkBytes];
+
+    // Tile order: split major; inside a split, groups of GM row tiles sweep
+    // all column tiles, so the workgroups resident on one XCD at a time share
+    // a few A and B panels in its L2.
+    const int logical = xcd_logical_id(blockIdx.x, gridDim.x);
+    const int per_split = tiles_m * tiles_n;
+    const int s = logical / per_split;
+    const int t = logical % per_split;
+    const int gm = min(GM, tiles_m);
+    const int group = t / (gm * tiles_n);
+    const int in_group = t % (gm * tiles_n);
+    const int rows_here = min(gm, tiles_m - group * gm);
+    const int mt = group * gm + in_group % rows_here;
+    const int nt = in_group / rows_here;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    const int r = lane & 31;
+    const int h = lane >> 5;
+
+    const int k0 = s * kps;
+    const int k1 = min(k0 + kps, K);
+    const int nchunks = (k1 - k0 + CK - 1) / CK;
+
+    // Load i of thread tid stages row i*(NT/8) + tid/8 into slot tid%8.  The
+    // row step NT/8 is a multiple of 16, so every load of a thread fetches
+    // the same swizzled piece; A rows come first (BM of them), then B rows.
+    static_assert((NT / 8) % 16 == 0 && BM % (NT / 8) == 0, "staging rows");
+    constexpr int ALOADS = BM / (NT / 8);
+    const size_t row_bytes = (size_t)K * ES;
+    const int piece = slot_of(tid >> 3, tid & 7);
+    const uint8_t* a_src = A + (size_t)(mt * BM + (tid >> 3)) * row_bytes + (size_t)k0 * ES;
+    const uint8_t* b_src = B + (size_t)(nt * BN + (tid >> 3)) * row_bytes + (size_t)k0 * ES;
+    const size_t step = (size_t)(NT / 8) * row_bytes;  // wave-uniform
+    auto half_chunk = [&](int c) { return k0 + c * CK + CK / 2 >= k1; };
+    u32x4 stg[LOADS];
+    auto load = [&](int c) {
+        const size_t off = (size_t)c * kChunkBytes + (piece & (half_chunk(c) ? 3 : 7)) * 16;
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i)
+            stg[i] = i < ALOADS ? *(const u32x4*)(a_src + i * step + off)
+                                : *(const u32x4*)(b_src + (i - ALOADS) * step + off);
+    };
+    // Stores the staged chunk c into LDS buffer `buf`.  In a half chunk the
+    // slots of pieces 4..7 are written as zeros, so the MFMA steps that read
+    // them add exactly 0 and the compute loop needs no branch.
+    auto stash = [&](int c, int buf) {
+        const bool zero = half_chunk(c) && piece >= 4;
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i)
+            *(u32x4*)(&smem[buf][0] + i * NT * 16 + tid * 16) = zero ? u32x4{} : stg[i];
+    };
+
+    f32x16 acc[MB][NB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x16{};
+
+    auto compute = [&](int buf) {
+        const uint8_t* lds = &smem[buf][0];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            u32x4 fa[MB], fb[NB];
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                const int row = wm * TM + mb * 32 + r;
+                fa[mb] = *(const u32x4*)(lds + row * kChunkBytes + slot_of(row, 2 * q + h) * 16);
+            }
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const int row = BM + wn * TN + nb * 32 + r;
+                fb[nb] = *(const u32x4*)(lds + row * kChunkBytes + slot_of(row, 2 * q + h) * 16);
+            }
+#pragma unroll
+            for (int e = 0; e < Op::kStepsPerPiece; ++e)
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb)
+                        acc[mb][nb] = Op::step(fa[mb], fb[nb], acc[mb][nb], e);
+        }
+    };
+
+    load(0);
+    stash(0, 0);
+    __syncthreads();
+    // Straight-line body (no branch around the accumulators): prefetch chunk
+    // c+1 into registers, multiply chunk c from LDS, stash chunk c+1.
+    int c = 0;
+    for (; c + 1 < nchunks; ++c) {
+        load(c + 1);
+        compute(c & 1);
+        stash(c + 1, (c + 1) & 1);
+        __syncthreads();
+    }
+    compute(c & 1);
+
+    // Register i of lane l holds row 8*(i/4) + 4*(l/32) + i%4, column l%32.
+    float* out = P + ((size_t)s * M + (size_t)mt * BM + wm * TM) * N + (size_t)nt * BN + wn * TN;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                out[(size_t)(mb * 32 + 8 * (i >> 2) + 4 * h + (i & 3)) * N + nb * 32 + r] = acc[mb][nb][i];
+}
+
+template <int DT, int BM, int BN, int WM, int WN>
+hipError_t launch_tiled(const void* A, const void* B, float* P, int64_t M, int64_t N, int64_t K,
+                        int64_t kps, int64_t splits, hipStream_t stream) {
+    const int tiles_m = (int)(M / BM), tiles_n = (int)(N / BN);
+    const dim3 grid((unsigned)(tiles_m * (int64_t)tiles_n * splits));
+    const dim3 block(WM * WN * 64);
+    const uint8_t* a = (const uint8_t*)A;
+    const uint8_t* b = (const uint8_t*)B;
+    int m = (int)M, n = (int)N, k = (int)K, kp = (int)kps;
+    void* args[] = {&a, &b, &P, &m, &n, &k, &kp, (void*)&tiles_m, (void*)&tiles_n};
+    return hipLaunchKernel((const void*)&gemm_bt_tiled<DT, BM, BN, WM, WN>, grid, block, args, 0,
+                           stream);
+}
+
+// Instantiated large-tile configurations: (BM, BN, WM, WN).
+#define SPLITK_TILED_CONFIGS(X) \
+    X(256, 256, 2, 2)           \
+    X(256, 128, 2, 2)           \
+    X(128, 128, 2, 2)
+
+template <int DT, int BM, int BN, int W, int D>
 hipError_t launch_wavek(const void* A, const void* B, float* P, int64_t M, int64_t N, int64_t K,
                         int64_t kps, int64_t splits, hipStream_t stream) {
     const int tiles_m = (int)(M / BM), tiles_n = (int)(N / BN);
@@ -213,42 +423,113 @@ hipError_t launch_wavek(const void* A, const void* B, float* P, int64_t M, int64
     const uint8_t* b = (const uint8_t*)B;
     int m = (int)M, n = (int)N, k = (int)K, kp = (int)kps;
     void* args[] = {&a, &b, &P, &m, &n, &k, &kp, (void*)&tiles_m, (void*)&tiles_n};
-    return hipLaunchKernel((const void*)&gemm_bt_wavek<DT, BM, BN, W>, grid, block, args, 0, stream);
+    return hipLaunchKernel((const void*)&gemm_bt_wavek<DT, BM, BN, W, D>, grid, block, args, 0,
+                           stream);
 }
+
+// The instantiated configurations: (BM, BN, waves, stages).
+#define SPLITK_WAVEK_CONFIGS(X) \
+    X(32, 32, 4, 1)             \
+    X(32, 32, 4, 2)             \
+    X(32, 32, 4, 4)             \
+    X(32, 64, 4, 1)             \
+    X(32, 64, 4, 2)             \
+    X(32, 64, 4, 4)             \
+    X(32, 32, 8, 1)             \
+    X(32, 32, 8, 2)             \
+    X(32, 64, 8, 1)             \
+    X(32, 64, 8, 2)             \
+    X(64, 64, 4, 2)             \
+    X(64, 64, 4, 4)
 
 template <int DT>
 hipError_t launch_dtype(const GemmPlan& p, const void* A, const void* B, float* P, int64_t M,
                         int64_t N, int64_t K, int64_t kps, int64_t splits, hipStream_t st) {
-    if (p.kind == kWaveK && p.waves == 4) {
-        if (p.bm == 32 && p.bn == 32) return launch_wavek<DT, 32, 32, 4>(A, B, P, M, N, K, kps, splits, st);
-        if (p.bm == 32 && p.bn == 64) return launch_wavek<DT, 32, 64, 4>(A, B, P, M, N, K, kps, splits, st);
+    if (p.kind == kWaveK) {
+#define X(cbm, cbn, cw, cd)                                                    \
+    if (p.bm == cbm && p.bn == cbn && p.waves == cw && p.stages == cd)        \
+        return launch_wavek<DT, cbm, cbn, cw, cd>(A, B, P, M, N, K, kps, splits, st);
+        SPLITK_WAVEK_CONFIGS(X)
+#undef X
+    }
+    if (p.kind == kTiled) {
+#define X(cbm, cbn, cwm, cwn)                                                     \
+    if (p.bm == cbm && p.bn == cbn && p.waves == cwm * cwn && p.stages == cwm)    \
+        return launch_tiled<DT, cbm, cbn, cwm, cwn>(A, B, P, M, N, K, kps, splits, st);
+        SPLITK_TILED_CONFIGS(X)
+#undef X
     }
     return hipErrorInvalidConfiguration;
 }
 
+bool wavek_config_exists(int bm, int bn, int w, int d) {
+#define X(cbm, cbn, cw, cd) \
+    if (bm == cbm && bn == cbn && w == cw && d == cd) return true;
+    SPLITK_WAVEK_CONFIGS(X)
+#undef X
+    return false;
+}
+
 }  // namespace
+
+bool tiled_config_exists(int bm, int bn, int wm, int wn) {
+#define X(cbm, cbn, cwm, cwn) \
+    if (bm == cbm && bn == cbn && wm == cwm && wn == cwn) return true;
+    SPLITK_TILED_CONFIGS(X)
+#undef X
+    return false;
+}
+
+// Optional override for tuning sweeps and tests: SPLITK_PLAN set to
+// "wavek,BM,BN,WAVES,STAGES" or "tiled,BM,BN,WM,WN" forces that instantiated
+// configuration wherever its tile divides the problem.  Read on every call
+// (a getenv is negligible next to a launch); unset or unknown values leave
+// the automatic choice in place.
+static bool forced_plan(int* kind, int* v) {
+    const char* e = getenv("SPLITK_PLAN");
+    char name[16] = {0};
+    if (!e || sscanf(e, "%15[a-z],%d,%d,%d,%d", name, &v[0], &v[1], &v[2], &v[3]) != 5) return false;
+    if (!strcmp(name, "wavek") && wavek_config_exists(v[0], v[1], v[2], v[3])) { *kind = kWaveK; return true; }
+    if (!strcmp(name, "tiled") && tiled_config_exists(v[0], v[1], v[2], v[3])) { *kind = kTiled; return true; }
+    return false;
+}
 
 GemmPlan plan_gemm(int dtype, int64_t M, int64_t N, int64_t K, int64_t kps, int64_t splits) {
     (void)K;
     const int64_t es = dtype == 0 ? 4 : 2;
-    // Pick the tile that moves the fewest bytes through the busiest CU: each
-    // workgroup streams (BM + BN) rows of its split, and workgroups beyond the
-    // 256 CUs queue behind the first round.
+    const int64_t ck = 128 / es;  // elements per 128-byte chunk
+    int fk, f[4];
+    if (forced_plan(&fk, f) && M % f[0] == 0 && N % f[1] == 0) {
+        const int64_t wg = (M / f[0]) * (N / f[1]) * splits;
+        if (fk == kTiled) return GemmPlan{kTiled, f[0], f[1], f[2] * f[3], f[2], wg, f[2] * f[3] * 64};
+        return GemmPlan{kWaveK, f[0], f[1], f[2], f[3], wg, f[2] * 64};
+    }
+    // Large problems: 256x256 tiles shared by four waves, when there are
+    // enough of them to give every CU several.
+    if (M % 256 == 0 && N % 256 == 0 && (M / 256) * (N / 256) * splits >= 512)
+        return GemmPlan{kTiled, 256, 256, 4, 2, (M / 256) * (N / 256) * splits, 256};
+    // Skinny problems.  Tile: the one that moves the fewest bytes through
+    // the busiest CU.  Each workgroup streams (BM + BN) rows of its split,
+    // and workgroups beyond the 256 CUs queue behind the first round.
     struct Cand { int bm, bn; };
     const Cand cands[] = {{32, 64}, {32, 32}};
-    GemmPlan best{kWaveK, 32, 32, 4, 0, 256};
+    int bm = 32, bn = 32;
     int64_t best_cost = -1;
     for (const Cand& c : cands) {
         if (M % c.bm || N % c.bn) continue;
         const int64_t wg = (M / c.bm) * (N / c.bn) * splits;
-        const int64_t rounds = (wg + 255) / 256;
-        const int64_t cost = rounds * (c.bm + c.bn) * kps * es;
-        if (best_cost < 0 || cost < best_cost) {
-            best_cost = cost;
-            best = GemmPlan{kWaveK, c.bm, c.bn, 4, wg, 4 * 64};
-        }
+        const int64_t cost = ((wg + 255) / 256) * (c.bm + c.bn) * kps * es;
+        if (best_cost < 0 || cost < best_cost) { best_cost = cost; bm = c.bm; bn = c.bn; }
     }
-    return best;
+    // Waves and stages: eight waves per workgroup (two per SIMD) measured
+    // best at every shape of this family; enough register stages to keep a
+    // wave's whole share of the split in flight, up to two.
+    const int64_t chunks = (kps + ck - 1) / ck;
+    const int w = 8;
+    int d = (chunks + w - 1) / w >= 2 ? 2 : 1;
+    while (d > 1 && !wavek_config_exists(bm, bn, w, d)) d /= 2;
+    const int64_t wg = (M / bm) * (N / bn) * splits;
+    return GemmPlan{kWaveK, bm, bn, w, d, wg, w * 64};
 }
 
 hipError_t launch_gemm_bt(const GemmPlan& plan, const void* A, const void* B, float* partials,

@@ -138,9 +138,12 @@ int splitk_describe(int64_t M, int64_t N, int64_t K, int64_t k_per_split, int64_
     if (st != SPLITK_OK) return st;
     const splitk::GemmPlan p = splitk::plan_gemm(dtype, M, N, K, k_per_split, splits);
     if (buf && len > 0) {
-        static const char* const names[] = {"wavek"};
-        snprintf(buf, (size_t)len, "%s bm%d bn%d waves%d block%d grid%lld", names[p.kind], p.bm, p.bn,
-                 p.waves, p.block, (long long)p.grid);
+        if (p.kind == splitk::kTiled)
+            snprintf(buf, (size_t)len, "tiled bm%d bn%d waves%dx%d block%d grid%lld", p.bm, p.bn,
+                     p.stages, p.waves / p.stages, p.block, (long long)p.grid);
+        else
+            snprintf(buf, (size_t)len, "wavek bm%d bn%d waves%d stages%d block%d grid%lld", p.bm, p.bn,
+                     p.waves, p.stages, p.block, (long long)p.grid);
     }
     return SPLITK_OK;
 }

@@ -13,11 +13,15 @@ enum GemmKind : int {
     // from global memory; the waves' accumulators are summed through LDS.
     // Suited to the skinny, short shapes (M <= 256) where the grid is small.
     kWaveK = 0,
+    // A BM x BN tile per workgroup; its waves split the tile (WM x WN) and
+    // share each staged chunk through double-buffered LDS.  For large
+    // problems with enough tiles to fill the chip.
+    kTiled = 1,
 };
 
 struct GemmPlan {
     int kind;
-    int bm, bn, waves;
+    int bm, bn, waves, stages;  // tiled kernels: stages = waves along M
     int64_t grid;  // workgroups
     int block;     // threads per workgroup
 };

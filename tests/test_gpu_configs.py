@@ -1,0 +1,115 @@
+"""Every instantiated GEMM kernel configuration against the binary64 reference.
+
+The automatic plan picks one configuration per shape; these tests force each
+instantiated one (through the SPLITK_PLAN override) on a small problem that
+spans several tiles, several chunks per wave, a steady-state pipeline pass
+and a short final split whose last chunk is half empty for 16-bit inputs.
+Acceptance as in test_gpu_parity.py (tolerances of "Aligned shared rows for
+pipelined NAX on CUDA", section "Contract and correctness").
+
+The configuration lists are read from the kernel source so that a newly
+instantiated configuration is tested without editing this file.
+"""
+from __future__ import annotations
+
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from conftest import gpu_available
+from split_dense_gemm_amd import inputs
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                   "split_dense_gemm_amd", "csrc", "gemm_bt.hip")
+
+
+def _configs(macro):
+    text = open(SRC).read()
+    body = text[text.index(f"#define {macro}(X)"):]
+    body = body[: body.index("\n\n")]
+    return [tuple(int(v) for v in m) for m in re.findall(r"X\((\d+), (\d+), (\d+), (\d+)\)", body)]
+
+
+WAVEK = _configs("SPLITK_WAVEK_CONFIGS")
+TILED = _configs("SPLITK_TILED_CONFIGS")
+
+
+def _shape(kind, cfg):
+    """(M, N, K, kps, splits) for a configuration."""
+    bm, bn = cfg[0], cfg[1]
+    if kind == "wavek":
+        # 37 chunks of 32 per split: odd, so 16-bit slices end in a half
+        # chunk; more chunks than waves x stages, so the pipeline loops.
+        return 3 * bm, max(2 * bn, 128), 2 * 1184 + 96, 1184, 3
+    return 2 * bm, 2 * bn, 2 * 608 + 32, 608, 3
+
+
+CASES = [("wavek", c) for c in WAVEK] + [("tiled", c) for c in TILED]
+
+
+def _plan_text(kind, cfg):
+    return f"{kind},{cfg[0]},{cfg[1]},{cfg[2]},{cfg[3]}"
+
+
+@pytest.fixture
+def forced(request):
+    kind, cfg = request.param
+    old = os.environ.get("SPLITK_PLAN")
+    os.environ["SPLITK_PLAN"] = _plan_text(kind, cfg)
+    yield kind, cfg
+    if old is None:
+        os.environ.pop("SPLITK_PLAN", None)
+    else:
+        os.environ["SPLITK_PLAN"] = old
+
+
+@pytest.mark.parametrize("forced", CASES, indirect=True, ids=lambda c: _plan_text(*c))
+def test_override_is_honoured(hip_lib, forced):
+    kind, cfg = forced
+    M, N, K, kps, S = _shape(kind, cfg)
+    text = hip_lib.describe(M, N, K, kps, S, 2)
+    assert text.startswith(kind) and f"bm{cfg[0]} bn{cfg[1]}" in text, text
+
+
+@pytest.mark.gpu
+@pytest.mark.skipif(not gpu_available(), reason="no GPU")
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("forced", CASES, indirect=True, ids=lambda c: _plan_text(*c))
+def test_config_parity(hip_lib, forced, dtype):
+    kind, cfg = forced
+    M, N, K, kps, S = _shape(kind, cfg)
+    print(f"case {_plan_text(kind, cfg)} {dtype} M{M} N{N} K{K} kps{kps} S{S}", flush=True)
+    dev = torch.device("cuda:0")
+    a, b = inputs.make_operands(M, N, K, dtype, seed=cfg[0] + cfg[1] + cfg[2] + cfg[3],
+                                zero_first_row=True, scale_last_row=True)
+    a64 = oracle.decode(inputs.stored_bits(a), dtype)
+    b64 = oracle.decode(inputs.stored_bits(b), dtype)
+    RP, DP, _ = oracle.splitk_partials(a64, b64, kps, S)
+    RC, DC, _ = oracle.gemm_bt(a64, b64)
+    pbuf = inputs.guarded_buffer(S * M * N, "nan").to(dev)
+    cbuf = inputs.guarded_buffer(M * N, "nan").to(dev)
+    hip_lib.gemm_bt_reduce(a.to(dev), b.to(dev), pbuf[: S * M * N].view(S, M, N),
+                           cbuf[: M * N].view(M, N), kps, S)
+    torch.cuda.synchronize()
+    p, c = pbuf.cpu().numpy(), cbuf.cpu().numpy()
+    guard = np.float32(inputs.GUARD_VALUE).view(np.uint32)
+    assert np.all(p[S * M * N:].view(np.uint32) == guard)
+    assert np.all(c[M * N:].view(np.uint32) == guard)
+    ep, _ = oracle.normalized_error(p[: S * M * N], RP, DP)
+    ec, _ = oracle.normalized_error(c[: M * N], RC, DC)
+    print(f"  partial err {ep:.3e}, final err {ec:.3e}", flush=True)
+    assert ep <= 1e-4
+    assert ec <= {"f32": 1e-4, "f16": 2e-3, "bf16": 2e-2}[dtype]
+    # Exact-arithmetic inputs: bit-for-bit.
+    ea, eb = inputs.exact_operands(M, N, K, dtype, seed=7)
+    ea64 = oracle.decode(inputs.stored_bits(ea), dtype)
+    eb64 = oracle.decode(inputs.stored_bits(eb), dtype)
+    EP, _, _ = oracle.splitk_partials(ea64, eb64, kps, S)
+    P = torch.empty(S, M, N, device=dev)
+    hip_lib.gemm_bt(ea.to(dev), eb.to(dev), P, kps, S)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(P.cpu().numpy().astype(np.float64), EP)

@@ -256,16 +256,30 @@ __global__ __launch_bounds__(W * 64) void gemm_bt_wavek(const uint8_t* __restric
     }
 }
 
+// s_waitcnt immediate that waits until at most n vector-memory operations
+// of this wave are outstanding (gfx9 encoding; the LDS and export counters
+// are left at their maxima, i.e. not waited on).
+#define SPLITK_VMCNT(n) ((((n) & 0xF) | ((((n) >> 4) & 3) << 14)) | 0x70 | 0xF00)
+
+// Workgroup barrier without the memory fence __syncthreads() adds (the
+// fence would wait for every load in flight, including the prefetches this
+// pipeline keeps in flight across barriers).  Each wave first waits for its
+// own LDS reads, so no read of a buffer is outstanding when another wave is
+// allowed to overwrite it; the "memory" clobber keeps the compiler from
+// moving LDS accesses across it.
+__device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // Large-tile kernel: each workgroup owns a BM x BN output tile of one split
-// and its WM x WN waves share every staged chunk.  Per 128-byte k-chunk the
-// whole workgroup loads BM + BN rows with coalesced 16-byte loads (eight
-// complete row segments per instruction), writes them to one of two swizzled
-// LDS buffers, and after one barrier every wave reads the fragments of its
-// (BM/WM) x (BN/WN) sub-tile while the next chunk's global loads are in
-// flight.  Accumulators are stored straight to the partial slab: for each
-// accumulator register the 32 lanes of a half-wave write 32 consecutive
-// floats of one row.
-template <int DT, int BM, int BN, int WM, int WN>
+// and its WM x WN waves share every staged chunk.  Chunks (128 bytes of each
+// of the BM + BN rows) travel from global memory straight into a ring of
+// NBUF LDS buffers (global_load_lds_dwordx4: no register staging and no
+// ds_write), NBUF - 1 chunks ahead of the one being multiplied.  One DMA
+// instruction of a wave fills eight whole 128-byte row segments, i.e. 1 KiB
+// of the buffer; the swizzle is applied on the global side (the lane that
+// fills slot j of row r fetches piece slot_of(r, j)).  Accumulators are
+// stored straight to the partial slab: for each accumulator register the 32
+// lanes of a half-wave write 32 consecutive floats of one row.
+template <int DT, int BM, int BN, int WM, int WN, int NBUF>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_bt_tiled(const uint8_t* __restrict__ A,
                                                               const uint8_t* __restrict__ B,
                                                               float* __restrict__ P, int M, int N,
@@ -274,14 +288,16 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bt_tiled(const uint8_t* __r
     using Op = Mfma<DT>;
     constexpr int ES = Op::kElemBytes;
     constexpr int CK = kChunkBytes / ES;
-    constexpr int NT = WM * WN * 64;          // threads
+    constexpr int NW = WM * WN;               // waves
     constexpr int ROWS = BM + BN;             // staged rows per chunk
-    constexpr int LOADS = ROWS * 8 / NT;      // 16-byte loads per thread per chunk
+    constexpr int BUF = ROWS * kChunkBytes;   // bytes per LDS buffer
+    constexpr int DPW = ROWS / 8 / NW;        // DMA instructions per wave per chunk
     constexpr int TM = BM / WM, TN = BN / WN; // per-wave sub-tile
     constexpr int MB = TM / 32, NB = TN / 32;
     constexpr int GM = 4;                     // row tiles per group of the tile order
-    static_assert(ROWS * 8 % NT == 0, "staging split");
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2][ROWS * kChunkBytes];
+    static_assert(ROWS % (8 * NW) == 0 && BM % 8 == 0, "staging split");
+    static_assert((NBUF - 2) * DPW < 64, "vmcnt range");
+    __shared__ __attribute__((aligned(16))) uint8_t smem[NBUF * BUF];
 
     // Tile order: split major; inside a split, groups of GM row tiles sweep
     // all column tiles, so the workgroups resident on one XCD at a time share
@@ -307,34 +323,33 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bt_tiled(const uint8_t* __r
     const int k0 = s * kps;
     const int k1 = min(k0 + kps, K);
     const int nchunks = (k1 - k0 + CK - 1) / CK;
-
-    // Load i of thread tid stages row i*(NT/8) + tid/8 into slot tid%8.  The
-    // row step NT/8 is a multiple of 16, so every load of a thread fetches
-    // the same swizzled piece; A rows come first (BM of them), then B rows.
-    static_assert((NT / 8) % 16 == 0 && BM % (NT / 8) == 0, "staging rows");
-    constexpr int ALOADS = BM / (NT / 8);
-    const size_t row_bytes = (size_t)K * ES;
-    const int piece = slot_of(tid >> 3, tid & 7);
-    const uint8_t* a_src = A + (size_t)(mt * BM + (tid >> 3)) * row_bytes + (size_t)k0 * ES;
-    const uint8_t* b_src = B + (size_t)(nt * BN + (tid >> 3)) * row_bytes + (size_t)k0 * ES;
-    const size_t step = (size_t)(NT / 8) * row_bytes;  // wave-uniform
     auto half_chunk = [&](int c) { return k0 + c * CK + CK / 2 >= k1; };
-    u32x4 stg[LOADS];
-    auto load = [&](int c) {
-        const size_t off = (size_t)c * kChunkBytes + (piece & (half_chunk(c) ? 3 : 7)) * 16;
+
+    // DMA instruction i of this wave fills rows 8*g .. 8*g+7 (g = i*NW + wave)
+    // of a buffer; this lane fills slot lane%8 of row 8*g + lane/8.
+    const size_t row_bytes = (size_t)K * ES;
+    const uint8_t* src[DPW];
+    int piece[DPW];
 #pragma unroll
-        for (int i = 0; i < LOADS; ++i)
-            stg[i] = i < ALOADS ? *(const u32x4*)(a_src + i * step + off)
-                                : *(const u32x4*)(b_src + (i - ALOADS) * step + off);
-    };
-    // Stores the staged chunk c into LDS buffer `buf`.  In a half chunk the
-    // slots of pieces 4..7 are written as zeros, so the MFMA steps that read
-    // them add exactly 0 and the compute loop needs no branch.
-    auto stash = [&](int c, int buf) {
-        const bool zero = half_chunk(c) && piece >= 4;
+    for (int i = 0; i < DPW; ++i) {
+        const int row = 8 * (i * NW + wave) + (lane >> 3);
+        src[i] = (row < BM ? A + (size_t)(mt * BM + row) * row_bytes
+                           : B + (size_t)(nt * BN + row - BM) * row_bytes) +
+                 (size_t)k0 * ES;
+        piece[i] = slot_of(row, lane & 7);
+    }
+    // Chunk c into ring slot c % NBUF.  In a half chunk the lanes meant for
+    // pieces 4..7 re-read pieces 0..3 (in bounds); those copies are finite
+    // and meet zero A fragments in compute().
+    auto dma = [&](int c) {
+        uint8_t* buf = smem + (c % NBUF) * BUF;
+        const int mask = half_chunk(c) ? 3 : 7;
+        const size_t off = (size_t)c * kChunkBytes;
 #pragma unroll
-        for (int i = 0; i < LOADS; ++i)
-            *(u32x4*)(&smem[buf][0] + i * NT * 16 + tid * 16) = zero ? u32x4{} : stg[i];
+        for (int i = 0; i < DPW; ++i)
+            __builtin_amdgcn_global_load_lds((const void*)(src[i] + off + (piece[i] & mask) * 16),
+                                             (__attribute__((address_space(3))) void*)(buf + (i * NW + wave) * 1024),
+                                             16, 0, 0);
     };
 
     f32x16 acc[MB][NB];
@@ -343,8 +358,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bt_tiled(const uint8_t* __r
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x16{};
 
-    auto compute = [&](int buf) {
-        const uint8_t* lds = &smem[buf][0];
+    auto compute = [&](int c) {
+        const uint8_t* lds = smem + (c % NBUF) * BUF;
+        const int steps = half_chunk(c) ? 2 : 4;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             u32x4 fa[MB], fb[NB];
@@ -352,6 +368,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bt_tiled(const uint8_t* __r
             for (int mb = 0; mb < MB; ++mb) {
                 const int row = wm * TM + mb * 32 + r;
                 fa[mb] = *(const u32x4*)(lds + row * kChunkBytes + slot_of(row, 2 * q + h) * 16);
+                if (q >= 2) fa[mb] = q < steps ? fa[mb] : u32x4{};
             }
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
@@ -368,19 +385,25 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bt_tiled(const uint8_t* __r
         }
     };
 
-    load(0);
-    stash(0, 0);
-    __syncthreads();
-    // Straight-line body (no branch around the accumulators): prefetch chunk
-    // c+1 into registers, multiply chunk c from LDS, stash chunk c+1.
+    // Prologue: the first NBUF - 1 chunks in flight.
+#pragma unroll
+    for (int j = 0; j < NBUF - 1; ++j)
+        if (j < nchunks) dma(j);
+    // Steady state: every pass issues one more chunk, so exactly NBUF - 2
+    // younger chunks (DPW loads each) are outstanding behind chunk c.
     int c = 0;
-    for (; c + 1 < nchunks; ++c) {
-        load(c + 1);
-        compute(c & 1);
-        stash(c + 1, (c + 1) & 1);
-        __syncthreads();
+    for (; c + NBUF - 1 < nchunks; ++c) {
+        __builtin_amdgcn_s_waitcnt(SPLITK_VMCNT((NBUF - 2) * DPW));
+        lds_barrier();  // chunk c complete for all waves; slot of chunk c-1 free
+        dma(c + NBUF - 1);
+        compute(c);
     }
-    compute(c & 1);
+    // Tail: no more loads to issue; wait for everything still in flight.
+    for (; c < nchunks; ++c) {
+        __builtin_amdgcn_s_waitcnt(SPLITK_VMCNT(0));
+        lds_barrier();
+        compute(c);
+    }
 
     // Register i of lane l holds row 8*(i/4) + 4*(l/32) + i%4, column l%32.
     float* out = P + ((size_t)s * M + (size_t)mt * BM + wm * TM) * N + (size_t)nt * BN + wn * TN;
@@ -393,7 +416,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bt_tiled(const uint8_t* __r
                 out[(size_t)(mb * 32 + 8 * (i >> 2) + 4 * h + (i & 3)) * N + nb * 32 + r] = acc[mb][nb][i];
 }
 
-template <int DT, int BM, int BN, int WM, int WN>
+template <int DT, int BM, int BN, int WM, int WN, int NBUF>
 hipError_t launch_tiled(const void* A, const void* B, float* P, int64_t M, int64_t N, int64_t K,
                         int64_t kps, int64_t splits, hipStream_t stream) {
     const int tiles_m = (int)(M / BM), tiles_n = (int)(N / BN);
@@ -403,15 +426,22 @@ hipError_t launch_tiled(const void* A, const void* B, float* P, int64_t M, int64
     const uint8_t* b = (const uint8_t*)B;
     int m = (int)M, n = (int)N, k = (int)K, kp = (int)kps;
     void* args[] = {&a, &b, &P, &m, &n, &k, &kp, (void*)&tiles_m, (void*)&tiles_n};
-    return hipLaunchKernel((const void*)&gemm_bt_tiled<DT, BM, BN, WM, WN>, grid, block, args, 0,
-                           stream);
+    return hipLaunchKernel((const void*)&gemm_bt_tiled<DT, BM, BN, WM, WN, NBUF>, grid, block, args,
+                           0, stream);
 }
 
-// Instantiated large-tile configurations: (BM, BN, WM, WN).
+// Instantiated large-tile configurations: (BM, BN, WM, WN); the LDS ring
+// holds as many chunk buffers as fit in 160 KiB, up to four.
 #define SPLITK_TILED_CONFIGS(X) \
     X(256, 256, 2, 2)           \
     X(256, 128, 2, 2)           \
+    X(256, 128, 2, 4)           \
     X(128, 128, 2, 2)
+
+template <int BM, int BN>
+constexpr int tiled_nbuf() {
+    return (160 * 1024) / ((BM + BN) * kChunkBytes) > 4 ? 4 : (160 * 1024) / ((BM + BN) * kChunkBytes);
+}
 
 template <int DT, int BM, int BN, int W, int D>
 hipError_t launch_wavek(const void* A, const void* B, float* P, int64_t M, int64_t N, int64_t K,
@@ -455,7 +485,7 @@ hipError_t launch_dtype(const GemmPlan& p, const void* A, const void* B, float* 
     if (p.kind == kTiled) {
 #define X(cbm, cbn, cwm, cwn)                                                     \
     if (p.bm == cbm && p.bn == cbn && p.waves == cwm * cwn && p.stages == cwm)    \
-        return launch_tiled<DT, cbm, cbn, cwm, cwn>(A, B, P, M, N, K, kps, splits, st);
+        return launch_tiled<DT, cbm, cbn, cwm, cwn, tiled_nbuf<cbm, cbn>()>(A, B, P, M, N, K, kps, splits, st);
         SPLITK_TILED_CONFIGS(X)
 #undef X
     }
@@ -504,10 +534,10 @@ GemmPlan plan_gemm(int dtype, int64_t M, int64_t N, int64_t K, int64_t kps, int6
         if (fk == kTiled) return GemmPlan{kTiled, f[0], f[1], f[2] * f[3], f[2], wg, f[2] * f[3] * 64};
         return GemmPlan{kWaveK, f[0], f[1], f[2], f[3], wg, f[2] * 64};
     }
-    // Large problems: 256x256 tiles shared by four waves, when there are
+    // Large problems: 256x128 tiles shared by eight waves, when there are
     // enough of them to give every CU several.
-    if (M % 256 == 0 && N % 256 == 0 && (M / 256) * (N / 256) * splits >= 512)
-        return GemmPlan{kTiled, 256, 256, 4, 2, (M / 256) * (N / 256) * splits, 256};
+    if (M % 256 == 0 && N % 128 == 0 && (M / 256) * (N / 128) * splits >= 1024)
+        return GemmPlan{kTiled, 256, 128, 8, 2, (M / 256) * (N / 128) * splits, 512};
     // Skinny problems.  Tile: the one that moves the fewest bytes through
     // the busiest CU.  Each workgroup streams (BM + BN) rows of its split,
     // and workgroups beyond the 256 CUs queue behind the first round.

@@ -534,10 +534,12 @@ GemmPlan plan_gemm(int dtype, int64_t M, int64_t N, int64_t K, int64_t kps, int6
         if (fk == kTiled) return GemmPlan{kTiled, f[0], f[1], f[2] * f[3], f[2], wg, f[2] * f[3] * 64};
         return GemmPlan{kWaveK, f[0], f[1], f[2], f[3], wg, f[2] * 64};
     }
-    // Large problems: 256x128 tiles shared by eight waves, when there are
-    // enough of them to give every CU several.
-    if (M % 256 == 0 && N % 128 == 0 && (M / 256) * (N / 128) * splits >= 1024)
-        return GemmPlan{kTiled, 256, 128, 8, 2, (M / 256) * (N / 128) * splits, 512};
+    // Large problems: 256x256 tiles (2x2 waves) when there is at least one
+    // per CU, else 256x128; these read the least L2 data per flop.
+    if (M % 256 == 0 && N % 256 == 0 && (M / 256) * (N / 256) * splits >= 256)
+        return GemmPlan{kTiled, 256, 256, 4, 2, (M / 256) * (N / 256) * splits, 256};
+    if (M % 256 == 0 && N % 128 == 0 && (M / 256) * (N / 128) * splits >= 256)
+        return GemmPlan{kTiled, 256, 128, 4, 2, (M / 256) * (N / 128) * splits, 256};
     // Skinny problems.  Tile: the one that moves the fewest bytes through
     // the busiest CU.  Each workgroup streams (BM + BN) rows of its split,
     // and workgroups beyond the 256 CUs queue behind the first round.

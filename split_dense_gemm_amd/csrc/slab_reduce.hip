@@ -8,13 +8,12 @@
 // additions, so the result is deterministic.
 //
 // It reads splits*M*N*4 bytes and writes M*N*4 bytes once each, so it is
-// bound by memory bandwidth.  Each lane owns one 16-byte word of the [M*N]
-// plane, issues all of its slab loads before the first add (so the loads of
-// every slab are in flight together) and writes that word once; consecutive
-// lanes touch consecutive words, so every load and store instruction of a
-// wave covers 1 KiB of contiguous memory.  The
-// slabs are read once and never again, so they are loaded non-temporally;
-// the output is stored normally.
+// bound by memory bandwidth.  A lane owns ITEMS 16-byte words of the [M*N]
+// plane, spaced one grid apart, and issues every slab load of all of them
+// before the first add, so ITEMS*S loads per lane are in flight together.
+// Consecutive lanes touch consecutive words: every load and store
+// instruction of a wave covers 1 KiB of contiguous memory.  The split count
+// is a compile-time constant for 1..8 so that no load sits behind a branch.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -27,37 +26,68 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBlock = 256;
 
-template <int MAXS>
+template <int S, int ITEMS>
 __global__ __launch_bounds__(kBlock) void slab_reduce_kernel(const f32x4* __restrict__ P,
                                                              f32x4* __restrict__ C, int splits,
                                                              int64_t plane4) {
-    const int64_t g = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-    if (g >= plane4) return;
-    if (MAXS > 0) {
-        // Small split counts: every slab load issued up front.
-        f32x4 v[MAXS > 0 ? MAXS : 1];
+    const int64_t stride = (int64_t)gridDim.x * kBlock;
+    const int64_t g0 = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (S > 0) {
+        f32x4 v[ITEMS][S > 0 ? S : 1];
 #pragma unroll
-        for (int s = 0; s < MAXS; ++s)
-            if (s < splits) v[s] = __builtin_nontemporal_load(P + (int64_t)s * plane4 + g);
-        f32x4 acc = v[0];
+        for (int it = 0; it < ITEMS; ++it) {
+            const int64_t g = g0 + it * stride;
+            if (g < plane4) {
 #pragma unroll
-        for (int s = 1; s < MAXS; ++s)
-            if (s < splits) acc += v[s];
-        C[g] = acc;
+                for (int s = 0; s < S; ++s) v[it][s] = P[s * plane4 + g];
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < ITEMS; ++it) {
+            const int64_t g = g0 + it * stride;
+            if (g < plane4) {
+                f32x4 acc = v[it][0];
+#pragma unroll
+                for (int s = 1; s < S; ++s) acc += v[it][s];
+                C[g] = acc;
+            }
+        }
     } else {
-        f32x4 acc = __builtin_nontemporal_load(P + g);
-        for (int s = 1; s < splits; ++s) acc += __builtin_nontemporal_load(P + (int64_t)s * plane4 + g);
-        C[g] = acc;
+        // Any other split count: ascending-s loop.
+        for (int it = 0; it < ITEMS; ++it) {
+            const int64_t g = g0 + it * stride;
+            if (g >= plane4) break;
+            f32x4 acc = P[g];
+            for (int s = 1; s < splits; ++s) acc += P[(int64_t)s * plane4 + g];
+            C[g] = acc;
+        }
     }
 }
 
-template <int MAXS>
+template <int S, int ITEMS>
 hipError_t launch(const float* partials, float* C, int splits, int64_t plane4, hipStream_t stream) {
-    const dim3 grid((unsigned)((plane4 + kBlock - 1) / kBlock));
+    const int64_t per_block = (int64_t)kBlock * ITEMS;
+    const dim3 grid((unsigned)((plane4 + per_block - 1) / per_block));
     const f32x4* p = (const f32x4*)partials;
     f32x4* c = (f32x4*)C;
     void* args[] = {&p, &c, &splits, &plane4};
-    return hipLaunchKernel((const void*)&slab_reduce_kernel<MAXS>, grid, dim3(kBlock), args, 0, stream);
+    return hipLaunchKernel((const void*)&slab_reduce_kernel<S, ITEMS>, grid, dim3(kBlock), args, 0,
+                           stream);
+}
+
+template <int ITEMS>
+hipError_t launch_items(const float* partials, float* C, int s, int64_t plane4, hipStream_t st) {
+    switch (s) {
+        case 1: return launch<1, ITEMS>(partials, C, s, plane4, st);
+        case 2: return launch<2, ITEMS>(partials, C, s, plane4, st);
+        case 3: return launch<3, ITEMS>(partials, C, s, plane4, st);
+        case 4: return launch<4, ITEMS>(partials, C, s, plane4, st);
+        case 5: return launch<5, ITEMS>(partials, C, s, plane4, st);
+        case 6: return launch<6, ITEMS>(partials, C, s, plane4, st);
+        case 7: return launch<7, ITEMS>(partials, C, s, plane4, st);
+        case 8: return launch<8, ITEMS>(partials, C, s, plane4, st);
+        default: return launch<0, ITEMS>(partials, C, s, plane4, st);
+    }
 }
 
 }  // namespace
@@ -66,10 +96,12 @@ hipError_t launch_slab_reduce(const float* partials, float* C, int64_t splits, i
                               hipStream_t stream) {
     const int64_t plane4 = M * N / 4;
     const int s = (int)splits;
-    if (s <= 2) return launch<2>(partials, C, s, plane4, stream);
-    if (s <= 4) return launch<4>(partials, C, s, plane4, stream);
-    if (s <= 8) return launch<8>(partials, C, s, plane4, stream);
-    return launch<0>(partials, C, s, plane4, stream);
+    // Four words per lane once the plane gives every CU several workgroups
+    // that way (measured faster for large planes); one word per lane
+    // otherwise, so that small planes still spread over all CUs.
+    if (plane4 >= (int64_t)256 * 4 * kBlock * 4)
+        return launch_items<4>(partials, C, s, plane4, stream);
+    return launch_items<1>(partials, C, s, plane4, stream);
 }
 
 }  // namespace splitk

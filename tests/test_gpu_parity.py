@@ -316,3 +316,20 @@ def test_error_statuses_with_real_buffers(sdg):
         a = torch.zeros(M, K, dtype=torch.bfloat16, device=dev)
         b = torch.zeros(N, K, dtype=torch.bfloat16, device=dev)
         sdg.gemm_bt(a, b, torch.zeros(3, M, N, device=dev), kps, 3)
+
+
+@pytest.mark.parametrize("S", [2, 3, 8, 11])
+def test_reduce_alone_large_plane(sdg, S):
+    """A plane large enough for the several-words-per-lane launch: sums of
+    small integers are exact, so C must equal the reference bit for bit."""
+    M, N = 2048, 2048
+    dev = torch.device("cuda:0")
+    gen = torch.Generator().manual_seed(100 + S)
+    ints = torch.randint(-1000, 1000, (S, M, N), generator=gen).float()
+    cbuf = inputs.guarded_buffer(M * N, "nan").to(dev)
+    sdg.reduce(ints.to(dev), cbuf[: M * N].view(M, N), S)
+    torch.cuda.synchronize()
+    got = cbuf.cpu().numpy()
+    ref, _, _ = oracle.slab_sum(ints.numpy())
+    np.testing.assert_array_equal(got[: M * N].astype(np.float64), ref.ravel())
+    assert np.all(got[M * N:].view(np.uint32) == GUARD_BITS)

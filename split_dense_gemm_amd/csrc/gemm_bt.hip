@@ -443,6 +443,193 @@ constexpr int tiled_nbuf() {
     return (160 * 1024) / ((BM + BN) * kChunkBytes) > 4 ? 4 : (160 * 1024) / ((BM + BN) * kChunkBytes);
 }
 
+// Skinny kernel with the last chunk by LDS DMA.  Same work split as
+// gemm_bt_wavek (waves take a split's chunks round-robin, partial tiles
+// summed through LDS), but each wave's last chunk travels from global memory
+// straight into a private LDS area (global_load_lds_dwordx4), issued after
+// the register loads of its earlier R chunks.  The last chunks are the ones
+// every wave receives at the same moment; writing them to LDS with ds_write
+// would queue eight waves' LDS writes at the very end.  Earlier chunks are
+// transposed into fragments block by block (32 rows at a time) through a
+// 4 KiB area, so one wave needs 4 KiB + one chunk of LDS.  A wave holds at
+// most R + 1 chunks; the host only picks this kernel when that is enough.
+template <int DT, int BM, int BN, int W, int R>
+__global__ __launch_bounds__(W * 64) void gemm_bt_wavek_dma(const uint8_t* __restrict__ A,
+                                                            const uint8_t* __restrict__ B,
+                                                            float* __restrict__ P, int M, int N,
+                                                            int K, int kps, int tiles_m,
+                                                            int tiles_n) {
+    using Op = Mfma<DT>;
+    constexpr int ES = Op::kElemBytes;
+    constexpr int CK = kChunkBytes / ES;
+    constexpr int MB = BM / 32, NB = BN / 32;
+    constexpr int ROWS = BM + BN;
+    constexpr int LOADS = ROWS / 8;
+    constexpr int BLOCK = 32 * kChunkBytes;          // one 32-row block of a chunk
+    constexpr int PITCH = BN + 4;
+    static_assert(LOADS < 64 && R * LOADS + LOADS < 64, "vmcnt range");
+    static_assert(W * BM * PITCH * 4 <= W * ROWS * kChunkBytes, "reduction tile fits the DMA area");
+    // Separate LDS objects for the transpose blocks and the DMA chunks, so
+    // the compiler can see that writing a transpose block does not have to
+    // wait for the DMA still in flight.  The reduction tile reuses the DMA
+    // area after a barrier.
+    __shared__ __attribute__((aligned(16))) uint8_t tr_lds[W][BLOCK];
+    __shared__ __attribute__((aligned(16))) uint8_t dma_lds[W][ROWS * kChunkBytes];
+    float (*red)[BM][PITCH] = reinterpret_cast<float (*)[BM][PITCH]>(&dma_lds[0][0]);
+
+    const int logical = xcd_logical_id(blockIdx.x, gridDim.x);
+    const int mt = logical % tiles_m;
+    const int rest = logical / tiles_m;
+    const int nt = rest % tiles_n;
+    const int s = rest / tiles_n;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int r = lane & 31;
+    const int h = lane >> 5;
+
+    const int k0 = s * kps;
+    const int k1 = min(k0 + kps, K);
+    const int nchunks = (k1 - k0 + CK - 1) / CK;
+    const int mine = wave < nchunks ? (nchunks - wave + W - 1) / W : 0;
+    // Chunk ids, clamped into range so that every load is unconditional; a
+    // wave with fewer than R + 1 chunks re-reads real chunks it never uses.
+    auto chunk_of = [&](int t) { return mine > 0 ? wave + min(max(t, 0), mine - 1) * W : 0; };
+    auto half_chunk = [&](int c) { return k0 + c * CK + CK / 2 >= k1; };
+
+    const size_t row_bytes = (size_t)K * ES;
+    const int lrow = lane >> 3;
+    const uint8_t* src[LOADS];
+    int piece[LOADS];
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+        const int row = 8 * i + lrow;
+        src[i] = (row < BM ? A + (size_t)(mt * BM + row) * row_bytes
+                           : B + (size_t)(nt * BN + row - BM) * row_bytes) +
+                 (size_t)k0 * ES;
+        piece[i] = slot_of(row, lane & 7);
+    }
+    uint8_t* tr = &tr_lds[wave][0];            // 4 KiB transpose block
+    uint8_t* dma_area = &dma_lds[wave][0];     // one whole chunk
+
+    f32x16 acc[MB][NB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x16{};
+
+    auto mfma_chunk = [&](const u32x4 (&fa)[MB][4], const u32x4 (&fb)[NB][4], int c) {
+        const int steps = half_chunk(c) ? 2 : 4;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int e = 0; e < Op::kStepsPerPiece; ++e)
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) {
+                    const u32x4 a = q >= 2 && q >= steps ? u32x4{} : fa[mb][q];
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = Op::step(a, fb[nb][q], acc[mb][nb], e);
+                }
+    };
+
+    // Register chunks: loads issued first.
+    u32x4 stg[R > 0 ? R : 1][LOADS];
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        const int c = chunk_of(j);
+        const size_t off = (size_t)c * kChunkBytes;
+        const int mask = half_chunk(c) ? 3 : 7;
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) stg[j][i] = *(const u32x4*)(src[i] + off + (piece[i] & mask) * 16);
+    }
+    // Last chunk: LDS DMA, issued after them (its rows 8i..8i+7 land at i KiB).
+    {
+        const int c = chunk_of(mine - 1);
+        const size_t off = (size_t)c * kChunkBytes;
+        const int mask = half_chunk(c) ? 3 : 7;
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i)
+            __builtin_amdgcn_global_load_lds((const void*)(src[i] + off + (piece[i] & mask) * 16),
+                                             (__attribute__((address_space(3))) void*)(dma_area + i * 1024),
+                                             16, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // Register chunks, oldest first: each 32-row block goes through the
+    // transpose area (ds_write four loads, ds_read four fragments).
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        if (j < mine - 1) {
+            u32x4 fa[MB][4], fb[NB][4];
+#pragma unroll
+            for (int blk = 0; blk < MB + NB; ++blk) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) *(u32x4*)(tr + i * 1024 + lane * 16) = stg[j][blk * 4 + i];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const u32x4 v = *(const u32x4*)(tr + r * kChunkBytes + slot_of(r, 2 * q + h) * 16);
+                    if (blk < MB) fa[blk][q] = v; else fb[blk - MB][q] = v;
+                }
+            }
+            mfma_chunk(fa, fb, chunk_of(j));
+        }
+    }
+    // The DMA chunk: wait for every load of this wave (it was issued last).
+    __builtin_amdgcn_s_waitcnt(SPLITK_VMCNT(0));
+    if (mine > 0) {
+        u32x4 fa[MB][4], fb[NB][4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                const int row = mb * 32 + r;
+                fa[mb][q] = *(const u32x4*)(dma_area + row * kChunkBytes + slot_of(row, 2 * q + h) * 16);
+            }
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const int row = BM + nb * 32 + r;
+                fb[nb][q] = *(const u32x4*)(dma_area + row * kChunkBytes + slot_of(row, 2 * q + h) * 16);
+            }
+        }
+        mfma_chunk(fa, fb, chunk_of(mine - 1));
+    }
+
+    __syncthreads();  // every wave is done with its LDS areas
+    // Operands were not swapped: register i of lane l holds row
+    // 8*(i/4) + 4*(l/32) + i%4, column l%32 of the block.
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                red[wave][mb * 32 + 8 * (i >> 2) + 4 * h + (i & 3)][nb * 32 + r] = acc[mb][nb][i];
+    __syncthreads();
+    constexpr int ROW4 = BN / 4;
+    float* out = P + ((size_t)s * M + (size_t)mt * BM) * N + (size_t)nt * BN;
+    for (int it = threadIdx.x; it < BM * ROW4; it += W * 64) {
+        const int row = it / ROW4;
+        const int col = (it % ROW4) * 4;
+        f32x4 v = *(const f32x4*)&red[0][row][col];
+#pragma unroll
+        for (int w = 1; w < W; ++w) v += *(const f32x4*)&red[w][row][col];
+        *(f32x4*)(out + (size_t)row * N + col) = v;
+    }
+}
+
+template <int DT, int BM, int BN, int W, int R>
+hipError_t launch_wavek_dma(const void* A, const void* B, float* P, int64_t M, int64_t N, int64_t K,
+                            int64_t kps, int64_t splits, hipStream_t stream) {
+    const int tiles_m = (int)(M / BM), tiles_n = (int)(N / BN);
+    const dim3 grid((unsigned)(tiles_m * (int64_t)tiles_n * splits));
+    const uint8_t* a = (const uint8_t*)A;
+    const uint8_t* b = (const uint8_t*)B;
+    int m = (int)M, n = (int)N, k = (int)K, kp = (int)kps;
+    void* args[] = {&a, &b, &P, &m, &n, &k, &kp, (void*)&tiles_m, (void*)&tiles_n};
+    return hipLaunchKernel((const void*)&gemm_bt_wavek_dma<DT, BM, BN, W, R>, grid, dim3(W * 64), args,
+                           0, stream);
+}
+
 template <int DT, int BM, int BN, int W, int D>
 hipError_t launch_wavek(const void* A, const void* B, float* P, int64_t M, int64_t N, int64_t K,
                         int64_t kps, int64_t splits, hipStream_t stream) {
@@ -458,6 +645,13 @@ hipError_t launch_wavek(const void* A, const void* B, float* P, int64_t M, int64
 }
 
 // The instantiated configurations: (BM, BN, waves, stages).
+// Instantiated (BM, BN, waves, register chunks) of the last-chunk-by-DMA kernel.
+#define SPLITK_WAVEKDMA_CONFIGS(X) \
+    X(32, 64, 8, 1)                \
+    X(32, 32, 8, 1)                \
+    X(32, 32, 8, 0)                \
+    X(32, 64, 8, 0)
+
 #define SPLITK_WAVEK_CONFIGS(X) \
     X(32, 32, 4, 1)             \
     X(32, 32, 4, 2)             \
@@ -482,6 +676,13 @@ hipError_t launch_dtype(const GemmPlan& p, const void* A, const void* B, float* 
         SPLITK_WAVEK_CONFIGS(X)
 #undef X
     }
+    if (p.kind == kWaveKDma) {
+#define X(cbm, cbn, cw, cr)                                                     \
+    if (p.bm == cbm && p.bn == cbn && p.waves == cw && p.stages == cr)          \
+        return launch_wavek_dma<DT, cbm, cbn, cw, cr>(A, B, P, M, N, K, kps, splits, st);
+        SPLITK_WAVEKDMA_CONFIGS(X)
+#undef X
+    }
     if (p.kind == kTiled) {
 #define X(cbm, cbn, cwm, cwn)                                                     \
     if (p.bm == cbm && p.bn == cbn && p.waves == cwm * cwn && p.stages == cwm)    \
@@ -490,6 +691,14 @@ hipError_t launch_dtype(const GemmPlan& p, const void* A, const void* B, float* 
 #undef X
     }
     return hipErrorInvalidConfiguration;
+}
+
+bool wavekdma_config_exists(int bm, int bn, int w, int r) {
+#define X(cbm, cbn, cw, cr) \
+    if (bm == cbm && bn == cbn && w == cw && r == cr) return true;
+    SPLITK_WAVEKDMA_CONFIGS(X)
+#undef X
+    return false;
 }
 
 bool wavek_config_exists(int bm, int bn, int w, int d) {
@@ -517,9 +726,10 @@ bool tiled_config_exists(int bm, int bn, int wm, int wn) {
 // the automatic choice in place.
 static bool forced_plan(int* kind, int* v) {
     const char* e = getenv("SPLITK_PLAN");
-    char name[16] = {0};
+    char name[16] = {0};  // "wavek", "wavekdma" or "tiled"
     if (!e || sscanf(e, "%15[a-z],%d,%d,%d,%d", name, &v[0], &v[1], &v[2], &v[3]) != 5) return false;
     if (!strcmp(name, "wavek") && wavek_config_exists(v[0], v[1], v[2], v[3])) { *kind = kWaveK; return true; }
+    if (!strcmp(name, "wavekdma") && wavekdma_config_exists(v[0], v[1], v[2], v[3])) { *kind = kWaveKDma; return true; }
     if (!strcmp(name, "tiled") && tiled_config_exists(v[0], v[1], v[2], v[3])) { *kind = kTiled; return true; }
     return false;
 }
@@ -528,11 +738,13 @@ GemmPlan plan_gemm(int dtype, int64_t M, int64_t N, int64_t K, int64_t kps, int6
     (void)K;
     const int64_t es = dtype == 0 ? 4 : 2;
     const int64_t ck = 128 / es;  // elements per 128-byte chunk
+    const int64_t max_chunks = (kps + ck - 1) / ck;  // chunks of the longest split
     int fk, f[4];
-    if (forced_plan(&fk, f) && M % f[0] == 0 && N % f[1] == 0) {
+    if (forced_plan(&fk, f) && M % f[0] == 0 && N % f[1] == 0 &&
+        (fk != kWaveKDma || max_chunks <= (int64_t)f[2] * (f[3] + 1))) {
         const int64_t wg = (M / f[0]) * (N / f[1]) * splits;
         if (fk == kTiled) return GemmPlan{kTiled, f[0], f[1], f[2] * f[3], f[2], wg, f[2] * f[3] * 64};
-        return GemmPlan{kWaveK, f[0], f[1], f[2], f[3], wg, f[2] * 64};
+        return GemmPlan{fk, f[0], f[1], f[2], f[3], wg, f[2] * 64};
     }
     // Large problems: 256x256 tiles (2x2 waves) when there is at least one
     // per CU, else 256x128; these read the least L2 data per flop.
@@ -556,11 +768,15 @@ GemmPlan plan_gemm(int dtype, int64_t M, int64_t N, int64_t K, int64_t kps, int6
     // Waves and stages: eight waves per workgroup (two per SIMD) measured
     // best at every shape of this family; enough register stages to keep a
     // wave's whole share of the split in flight, up to two.
-    const int64_t chunks = (kps + ck - 1) / ck;
+    const int64_t chunks = max_chunks;
     const int w = 8;
-    int d = (chunks + w - 1) / w >= 2 ? 2 : 1;
-    while (d > 1 && !wavek_config_exists(bm, bn, w, d)) d /= 2;
     const int64_t wg = (M / bm) * (N / bn) * splits;
+    // Each wave's last chunk by LDS DMA whenever a wave has at most two.
+    const int64_t per_wave = (chunks + w - 1) / w;
+    if (per_wave <= 2 && wavekdma_config_exists(bm, bn, w, (int)per_wave - 1))
+        return GemmPlan{kWaveKDma, bm, bn, w, (int)per_wave - 1, wg, w * 64};
+    int d = per_wave >= 2 ? 2 : 1;
+    while (d > 1 && !wavek_config_exists(bm, bn, w, d)) d /= 2;
     return GemmPlan{kWaveK, bm, bn, w, d, wg, w * 64};
 }
 

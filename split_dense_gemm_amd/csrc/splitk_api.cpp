@@ -142,8 +142,9 @@ int splitk_describe(int64_t M, int64_t N, int64_t K, int64_t k_per_split, int64_
             snprintf(buf, (size_t)len, "tiled bm%d bn%d waves%dx%d block%d grid%lld", p.bm, p.bn,
                      p.stages, p.waves / p.stages, p.block, (long long)p.grid);
         else
-            snprintf(buf, (size_t)len, "wavek bm%d bn%d waves%d stages%d block%d grid%lld", p.bm, p.bn,
-                     p.waves, p.stages, p.block, (long long)p.grid);
+            snprintf(buf, (size_t)len, "%s bm%d bn%d waves%d stages%d block%d grid%lld",
+                     p.kind == splitk::kWaveKDma ? "wavekdma" : "wavek", p.bm, p.bn, p.waves, p.stages,
+                     p.block, (long long)p.grid);
     }
     return SPLITK_OK;
 }

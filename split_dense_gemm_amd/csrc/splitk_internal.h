@@ -17,6 +17,9 @@ enum GemmKind : int {
     // share each staged chunk through double-buffered LDS.  For large
     // problems with enough tiles to fill the chip.
     kTiled = 1,
+    // As kWaveK, but each wave's last chunk travels by LDS DMA; for splits
+    // short enough that a wave holds at most STAGES + 1 chunks.
+    kWaveKDma = 2,
 };
 
 struct GemmPlan {

@@ -70,7 +70,7 @@ def test_describe_checks_shape_and_split(hip_lib, args, status):
     got = hip_lib.load().splitk_describe(*args, buf, len(buf))
     assert got == status
     if status == OK:
-        assert buf.value.split()[0] in (b"wavek", b"tiled")
+        assert buf.value.split()[0] in (b"wavek", b"wavekdma", b"tiled")
 
 
 def test_plan_for_each_workload(hip_lib):

@@ -35,6 +35,7 @@ def _configs(macro):
 
 
 WAVEK = _configs("SPLITK_WAVEK_CONFIGS")
+WAVEKDMA = _configs("SPLITK_WAVEKDMA_CONFIGS")
 TILED = _configs("SPLITK_TILED_CONFIGS")
 
 
@@ -45,10 +46,18 @@ def _shape(kind, cfg):
         # 37 chunks of 32 per split: odd, so 16-bit slices end in a half
         # chunk; more chunks than waves x stages, so the pipeline loops.
         return 3 * bm, max(2 * bn, 128), 2 * 1184 + 96, 1184, 3
+    if kind == "wavekdma":
+        # At most waves x (register chunks + 1) chunks per split (F32 chunks
+        # hold 32 elements, 16-bit ones 64); odd multiples of 32 end 16-bit
+        # slices in a half chunk, and the short last split leaves some waves
+        # with fewer chunks than others.
+        kps = 32 * (7 if cfg[3] == 0 else 15)
+        return 3 * bm, max(2 * bn, 128), 2 * kps + 96, kps, 3
     return 2 * bm, 2 * bn, 2 * 608 + 32, 608, 3
 
 
-CASES = [("wavek", c) for c in WAVEK] + [("tiled", c) for c in TILED]
+CASES = ([("wavek", c) for c in WAVEK] + [("wavekdma", c) for c in WAVEKDMA] +
+         [("tiled", c) for c in TILED])
 
 
 def _plan_text(kind, cfg):

@@ -106,6 +106,27 @@ int splitk_gemm_bt_reduce(const void* A, const void* B, float* partials, float* 
                           int64_t N, int64_t K, int64_t k_per_split, int64_t splits, int dtype,
                           void* stream);
 
+/*
+ * Typed final output: the same slab sum, formed in F32 and then rounded to
+ * `out_dtype` (a splitk_dtype; round to nearest, ties to even).  This is the
+ * step downstream of the accumulation pass that the per-type final-output
+ * tolerances of the pages suggest (first page, "Contract and correctness";
+ * second page, "Performance method": F32 1e-4, F16 2e-3, BF16 2e-2).
+ *   C   [M,N] elements of out_dtype, written in full.
+ * Other arguments and errors as for splitk_reduce; SPLITK_ERR_DTYPE for an
+ * unknown out_dtype.
+ */
+int splitk_reduce_typed(const float* partials, void* C, int64_t splits, int64_t M, int64_t N,
+                        int out_dtype, void* stream);
+
+/*
+ * splitk_gemm_bt then splitk_reduce_typed on the same stream.  C is [M,N] of
+ * out_dtype; all arguments are checked before either kernel is enqueued.
+ */
+int splitk_gemm_bt_reduce_typed(const void* A, const void* B, float* partials, void* C, int64_t M,
+                                int64_t N, int64_t K, int64_t k_per_split, int64_t splits,
+                                int dtype, int out_dtype, void* stream);
+
 /* Static text for a status code ("unknown status" for anything else). */
 const char* splitk_status_str(int status);
 

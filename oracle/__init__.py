@@ -6,6 +6,7 @@ baseline leg of bench.py.  The product library never imports or links it.
 from .ref import (  # noqa: F401
     build,
     decode,
+    encode,
     gemm_bt,
     normalized_error,
     sampled,

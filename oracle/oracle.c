@@ -91,6 +91,63 @@ int oracle_decode(const void* src, int dtype, int64_t n, double* dst) {
     return 0;
 }
 
+/* ---------------------------------------------------------------- encoding */
+
+/* Round a binary64 value to nearest, ties to even, in a binary format with
+ * p significand bits (hidden bit included), minimum normal exponent emin and
+ * maximum exponent emax, and return its bits (sign, exponent field, fraction
+ * field; bias = emax).  Written from the IEEE-754 definition: the result is
+ * the representable value nearest x, the one with an even last significand
+ * bit on a tie, infinity if that nearest value would exceed the largest
+ * finite one.  Subnormals are kept. */
+static uint32_t encode_rne(double x, int p, int emin, int emax) {
+    const uint32_t sign = signbit(x) ? 1u : 0u;
+    const int ebits = (emax == 127) ? 8 : 5;
+    const uint32_t sign_shift = (uint32_t)(ebits + p - 1);
+    if (isnan(x)) return (sign << sign_shift) | (((1u << ebits) - 1) << (p - 1)) | (1u << (p - 2));
+    double a = fabs(x);
+    if (a == 0.0) return sign << sign_shift;
+    if (isinf(a)) return (sign << sign_shift) | (((1u << ebits) - 1) << (p - 1));
+    int e;
+    frexp(a, &e);            /* a = f * 2^e, f in [0.5, 1): leading bit at 2^(e-1) */
+    int lead = e - 1;
+    if (lead < emin) lead = emin;           /* subnormal range: fixed quantum */
+    const double q = ldexp(1.0, lead - (p - 1));
+    double n = nearbyint(a / q);            /* a/q is exact: q is a power of two */
+    /* A carry can lift n to 2^p: that is the next binade's smallest value. */
+    if (n >= ldexp(1.0, p)) { n /= 2; lead += 1; }
+    if (lead > emax) return (sign << sign_shift) | (((1u << ebits) - 1) << (p - 1));  /* inf */
+    uint32_t exp_field, frac;
+    if (n < ldexp(1.0, p - 1)) {            /* subnormal (lead == emin) or zero */
+        exp_field = 0;
+        frac = (uint32_t)n;
+    } else {
+        exp_field = (uint32_t)(lead + emax);
+        frac = (uint32_t)(n - ldexp(1.0, p - 1));
+    }
+    return (sign << sign_shift) | (exp_field << (p - 1)) | frac;
+}
+
+/* Rounds n binary64 values to `dtype` (ties to even) and stores their bits:
+ * uint32 for F32, uint16 for F16 and BF16.  Returns 0, or -1 for an unknown
+ * dtype. */
+int oracle_encode(const double* src, int dtype, int64_t n, void* dst) {
+    int64_t t;
+    if (dtype == ORACLE_F32) {
+        uint32_t* d = (uint32_t*)dst;
+        for (t = 0; t < n; ++t) d[t] = encode_rne(src[t], 24, -126, 127);
+    } else if (dtype == ORACLE_F16) {
+        uint16_t* d = (uint16_t*)dst;
+        for (t = 0; t < n; ++t) d[t] = (uint16_t)encode_rne(src[t], 11, -14, 15);
+    } else if (dtype == ORACLE_BF16) {
+        uint16_t* d = (uint16_t*)dst;
+        for (t = 0; t < n; ++t) d[t] = (uint16_t)encode_rne(src[t], 8, -126, 127);
+    } else {
+        return -1;
+    }
+    return 0;
+}
+
 /* ------------------------------------------------------------ split bounds */
 
 /* Bounds of split s: [k0, k1) with k1 clamped to K (same sections as above). */

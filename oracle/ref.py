@@ -52,6 +52,7 @@ def _load():
     P = ctypes.c_void_p
     I64 = ctypes.c_int64
     lib.oracle_decode.argtypes = [P, ctypes.c_int, I64, P]
+    lib.oracle_encode.argtypes = [P, ctypes.c_int, I64, P]
     lib.oracle_splitk_partials.argtypes = [P, P, I64, I64, I64, I64, I64, P, P, ctypes.c_int]
     lib.oracle_gemm_bt.argtypes = [P, P, I64, I64, I64, P, P, ctypes.c_int]
     lib.oracle_slab_sum.argtypes = [P, I64, I64, I64, P, P, ctypes.c_int]
@@ -83,6 +84,19 @@ def decode(bits: np.ndarray, dtype: str) -> np.ndarray:
         raise TypeError(f"{dtype} bits must be {want.__name__}, got {bits.dtype}")
     out = np.empty(bits.shape, dtype=np.float64)
     rc = _load().oracle_decode(_ptr(bits), _DTYPE[dtype], bits.size, _ptr(out))
+    if rc != 0:
+        raise ValueError(dtype)
+    return out
+
+
+def encode(values: np.ndarray, dtype: str) -> np.ndarray:
+    """Bits of binary64 values rounded to `dtype` (nearest, ties to even).
+
+    Used for typed final outputs: the split-K sum rounded to F16 or BF16.
+    """
+    values = np.ascontiguousarray(values, dtype=np.float64)
+    out = np.empty(values.shape, dtype=np.uint32 if dtype == "f32" else np.uint16)
+    rc = _load().oracle_encode(_ptr(values), _DTYPE[dtype], values.size, _ptr(out))
     if rc != 0:
         raise ValueError(dtype)
     return out

@@ -60,6 +60,10 @@ def load():
     lib.splitk_reduce.restype = I
     lib.splitk_gemm_bt_reduce.argtypes = [P, P, P, P, I64, I64, I64, I64, I64, I, P]
     lib.splitk_gemm_bt_reduce.restype = I
+    lib.splitk_reduce_typed.argtypes = [P, P, I64, I64, I64, I, P]
+    lib.splitk_reduce_typed.restype = I
+    lib.splitk_gemm_bt_reduce_typed.argtypes = [P, P, P, P, I64, I64, I64, I64, I64, I, I, P]
+    lib.splitk_gemm_bt_reduce_typed.restype = I
     lib.splitk_status_str.argtypes = [I]
     lib.splitk_status_str.restype = ctypes.c_char_p
     lib.splitk_describe.argtypes = [I64, I64, I64, I64, I64, I, ctypes.c_char_p, I64]
@@ -126,25 +130,47 @@ def gemm_bt(A: torch.Tensor, B: torch.Tensor, partials: torch.Tensor, k_per_spli
     return partials
 
 
+def _out(t: torch.Tensor, numel: int) -> int:
+    _dev(t, "C")
+    if t.dtype not in DTYPE_CODE:
+        raise ValueError(f"C must be float32, float16 or bfloat16, got {t.dtype}")
+    if t.numel() != numel:
+        raise ValueError(f"C must hold {numel} elements, got {t.numel()}")
+    return DTYPE_CODE[t.dtype]
+
+
 def reduce(partials: torch.Tensor, C: torch.Tensor, splits: int, stream=None) -> torch.Tensor:
-    """C[i,j] = sum over s of partials[s,i,j] (see splitk.h)."""
+    """C[i,j] = sum over s of partials[s,i,j] (see splitk.h).  A float16 or
+    bfloat16 C receives the F32 sum rounded to nearest, ties to even."""
     if C.dim() != 2:
         raise ValueError("C must be [M,N]")
     M, N = C.shape
-    _f32_out(C, "C", M * N)
+    out = _out(C, M * N)
     _f32_out(partials, "partials", splits * M * N)
-    _check(load().splitk_reduce(partials.data_ptr(), C.data_ptr(), int(splits), M, N, _stream(stream)))
+    if out == 0:
+        _check(load().splitk_reduce(partials.data_ptr(), C.data_ptr(), int(splits), M, N,
+                                    _stream(stream)))
+    else:
+        _check(load().splitk_reduce_typed(partials.data_ptr(), C.data_ptr(), int(splits), M, N, out,
+                                          _stream(stream)))
     return C
 
 
 def gemm_bt_reduce(A: torch.Tensor, B: torch.Tensor, partials: torch.Tensor, C: torch.Tensor,
                    k_per_split: int, splits: int, stream=None) -> torch.Tensor:
-    """The split-K GEMM and the slab sum back to back on one stream (see splitk.h)."""
+    """The split-K GEMM and the slab sum back to back on one stream (see
+    splitk.h); C may be float32, float16 or bfloat16."""
     M, N, K, dt = _operands(A, B)
     _f32_out(partials, "partials", splits * M * N)
-    _f32_out(C, "C", M * N)
-    _check(load().splitk_gemm_bt_reduce(A.data_ptr(), B.data_ptr(), partials.data_ptr(), C.data_ptr(),
-                                        M, N, K, int(k_per_split), int(splits), dt, _stream(stream)))
+    out = _out(C, M * N)
+    if out == 0:
+        _check(load().splitk_gemm_bt_reduce(A.data_ptr(), B.data_ptr(), partials.data_ptr(),
+                                            C.data_ptr(), M, N, K, int(k_per_split), int(splits), dt,
+                                            _stream(stream)))
+    else:
+        _check(load().splitk_gemm_bt_reduce_typed(A.data_ptr(), B.data_ptr(), partials.data_ptr(),
+                                                  C.data_ptr(), M, N, K, int(k_per_split), int(splits),
+                                                  dt, out, _stream(stream)))
     return C
 
 

@@ -29,9 +29,11 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 int element_bytes(int dtype) { return dtype == SPLITK_F32 ? 4 : 2; }
 
+bool valid_dtype(int dtype) { return dtype == SPLITK_F32 || dtype == SPLITK_F16 || dtype == SPLITK_BF16; }
+
 // Shape, split and size checks shared by the GEMM entry points.
 int check_gemm_shape(int64_t M, int64_t N, int64_t K, int64_t kps, int64_t splits, int dtype) {
-    if (dtype != SPLITK_F32 && dtype != SPLITK_F16 && dtype != SPLITK_BF16) return SPLITK_ERR_DTYPE;
+    if (!valid_dtype(dtype)) return SPLITK_ERR_DTYPE;
     if (M <= 0 || N <= 0 || K <= 0 || kps <= 0) return SPLITK_ERR_SHAPE;
     if (M % 32 || K % 32 || kps % 32 || N % 64) return SPLITK_ERR_SHAPE;
     if (M >= kMaxElems || N >= kMaxElems || K >= kMaxElems || kps >= kMaxElems) return SPLITK_ERR_RANGE;
@@ -45,9 +47,9 @@ int check_gemm_shape(int64_t M, int64_t N, int64_t K, int64_t kps, int64_t split
 }
 
 // Pointer checks: alignment, then overlap of outputs with everything else.
-// C may be NULL (GEMM alone).
-int check_gemm_pointers(const void* A, const void* B, const float* P, const float* C, int64_t M,
-                        int64_t N, int64_t K, int64_t splits, int dtype) {
+// C may be NULL (GEMM alone); c_es is the byte size of one C element.
+int check_gemm_pointers(const void* A, const void* B, const float* P, const void* C, int64_t M,
+                        int64_t N, int64_t K, int64_t splits, int dtype, int64_t c_es) {
     if (!aligned16(A) || !aligned16(B) || !aligned16(P) || (C && !aligned16(C))) return SPLITK_ERR_ALIGN;
     const int64_t es = element_bytes(dtype);
     const Range ra{(uintptr_t)A, (uintptr_t)A + (uintptr_t)(M * K * es)};
@@ -55,21 +57,22 @@ int check_gemm_pointers(const void* A, const void* B, const float* P, const floa
     const Range rp{(uintptr_t)P, (uintptr_t)P + (uintptr_t)(splits * M * N * 4)};
     if (overlaps(rp, ra) || overlaps(rp, rb)) return SPLITK_ERR_ALIAS;
     if (C) {
-        const Range rc{(uintptr_t)C, (uintptr_t)C + (uintptr_t)(M * N * 4)};
+        const Range rc{(uintptr_t)C, (uintptr_t)C + (uintptr_t)(M * N * c_es)};
         if (overlaps(rc, ra) || overlaps(rc, rb) || overlaps(rc, rp)) return SPLITK_ERR_ALIAS;
     }
     return SPLITK_OK;
 }
 
-int check_reduce(const float* P, const float* C, int64_t splits, int64_t M, int64_t N) {
+int check_reduce(const float* P, const void* C, int64_t splits, int64_t M, int64_t N, int out_dtype) {
     if (!P || !C) return SPLITK_ERR_NULL;
+    if (!valid_dtype(out_dtype)) return SPLITK_ERR_DTYPE;
     if (M <= 0 || N <= 0 || M % 32 || N % 64) return SPLITK_ERR_SHAPE;
     if (splits < 1) return SPLITK_ERR_SPLIT;
     if (M >= kMaxElems || N >= kMaxElems || splits >= kMaxElems) return SPLITK_ERR_RANGE;
     if (M * N >= kMaxElems || splits * (M * N) >= kMaxElems) return SPLITK_ERR_RANGE;
     if (!aligned16(P) || !aligned16(C)) return SPLITK_ERR_ALIGN;
     const Range rp{(uintptr_t)P, (uintptr_t)P + (uintptr_t)(splits * M * N * 4)};
-    const Range rc{(uintptr_t)C, (uintptr_t)C + (uintptr_t)(M * N * 4)};
+    const Range rc{(uintptr_t)C, (uintptr_t)C + (uintptr_t)(M * N * element_bytes(out_dtype))};
     if (overlaps(rp, rc)) return SPLITK_ERR_ALIAS;
     return SPLITK_OK;
 }
@@ -101,7 +104,7 @@ int splitk_gemm_bt(const void* A, const void* B, float* partials, int64_t M, int
     if (!A || !B || !partials) return SPLITK_ERR_NULL;
     int st = check_gemm_shape(M, N, K, k_per_split, splits, dtype);
     if (st != SPLITK_OK) return st;
-    st = check_gemm_pointers(A, B, partials, nullptr, M, N, K, splits, dtype);
+    st = check_gemm_pointers(A, B, partials, nullptr, M, N, K, splits, dtype, 0);
     if (st != SPLITK_OK) return st;
     const splitk::GemmPlan plan = splitk::plan_gemm(dtype, M, N, K, k_per_split, splits);
     hipError_t e = splitk::launch_gemm_bt(plan, A, B, partials, M, N, K, k_per_split, splits, dtype,
@@ -109,27 +112,40 @@ int splitk_gemm_bt(const void* A, const void* B, float* partials, int64_t M, int
     return e == hipSuccess ? SPLITK_OK : SPLITK_ERR_LAUNCH;
 }
 
-int splitk_reduce(const float* partials, float* C, int64_t splits, int64_t M, int64_t N, void* stream) {
-    int st = check_reduce(partials, C, splits, M, N);
+int splitk_reduce_typed(const float* partials, void* C, int64_t splits, int64_t M, int64_t N,
+                        int out_dtype, void* stream) {
+    int st = check_reduce(partials, C, splits, M, N, out_dtype);
     if (st != SPLITK_OK) return st;
-    hipError_t e = splitk::launch_slab_reduce(partials, C, splits, M, N, (hipStream_t)stream);
+    hipError_t e = splitk::launch_slab_reduce(partials, C, splits, M, N, out_dtype, (hipStream_t)stream);
+    return e == hipSuccess ? SPLITK_OK : SPLITK_ERR_LAUNCH;
+}
+
+int splitk_reduce(const float* partials, float* C, int64_t splits, int64_t M, int64_t N, void* stream) {
+    return splitk_reduce_typed(partials, C, splits, M, N, SPLITK_F32, stream);
+}
+
+int splitk_gemm_bt_reduce_typed(const void* A, const void* B, float* partials, void* C, int64_t M,
+                                int64_t N, int64_t K, int64_t k_per_split, int64_t splits, int dtype,
+                                int out_dtype, void* stream) {
+    if (!A || !B || !partials || !C) return SPLITK_ERR_NULL;
+    int st = check_gemm_shape(M, N, K, k_per_split, splits, dtype);
+    if (st != SPLITK_OK) return st;
+    if (!valid_dtype(out_dtype)) return SPLITK_ERR_DTYPE;
+    st = check_gemm_pointers(A, B, partials, C, M, N, K, splits, dtype, element_bytes(out_dtype));
+    if (st != SPLITK_OK) return st;
+    const splitk::GemmPlan plan = splitk::plan_gemm(dtype, M, N, K, k_per_split, splits);
+    hipError_t e = splitk::launch_gemm_bt(plan, A, B, partials, M, N, K, k_per_split, splits, dtype,
+                                          (hipStream_t)stream);
+    if (e != hipSuccess) return SPLITK_ERR_LAUNCH;
+    e = splitk::launch_slab_reduce(partials, C, splits, M, N, out_dtype, (hipStream_t)stream);
     return e == hipSuccess ? SPLITK_OK : SPLITK_ERR_LAUNCH;
 }
 
 int splitk_gemm_bt_reduce(const void* A, const void* B, float* partials, float* C, int64_t M,
                           int64_t N, int64_t K, int64_t k_per_split, int64_t splits, int dtype,
                           void* stream) {
-    if (!A || !B || !partials || !C) return SPLITK_ERR_NULL;
-    int st = check_gemm_shape(M, N, K, k_per_split, splits, dtype);
-    if (st != SPLITK_OK) return st;
-    st = check_gemm_pointers(A, B, partials, C, M, N, K, splits, dtype);
-    if (st != SPLITK_OK) return st;
-    const splitk::GemmPlan plan = splitk::plan_gemm(dtype, M, N, K, k_per_split, splits);
-    hipError_t e = splitk::launch_gemm_bt(plan, A, B, partials, M, N, K, k_per_split, splits, dtype,
-                                          (hipStream_t)stream);
-    if (e != hipSuccess) return SPLITK_ERR_LAUNCH;
-    e = splitk::launch_slab_reduce(partials, C, splits, M, N, (hipStream_t)stream);
-    return e == hipSuccess ? SPLITK_OK : SPLITK_ERR_LAUNCH;
+    return splitk_gemm_bt_reduce_typed(A, B, partials, C, M, N, K, k_per_split, splits, dtype,
+                                       SPLITK_F32, stream);
 }
 
 int splitk_describe(int64_t M, int64_t N, int64_t K, int64_t k_per_split, int64_t splits, int dtype,

@@ -36,7 +36,8 @@ hipError_t launch_gemm_bt(const GemmPlan& plan, const void* A, const void* B, fl
                           int64_t M, int64_t N, int64_t K, int64_t kps, int64_t splits, int dtype,
                           hipStream_t stream);
 
-hipError_t launch_slab_reduce(const float* partials, float* C, int64_t splits, int64_t M, int64_t N,
-                              hipStream_t stream);
+// out_dtype: 0 F32, 1 F16, 2 BF16 (the sum is formed in F32, then rounded).
+hipError_t launch_slab_reduce(const float* partials, void* C, int64_t splits, int64_t M, int64_t N,
+                              int out_dtype, hipStream_t stream);
 
 }  // namespace splitk

@@ -116,13 +116,16 @@ def exact_operands(M: int, N: int, K: int, dtype: str, seed: int):
     return a.to(DTYPES[dtype]).contiguous(), b.to(DTYPES[dtype]).contiguous()
 
 
-def guarded_buffer(n: int, poison: str = "seven") -> torch.Tensor:
-    """F32 CPU buffer of n poisoned elements plus GUARD_COUNT trailing guards."""
-    buf = torch.empty(n + GUARD_COUNT, dtype=torch.float32)
+def guarded_buffer(n: int, poison: str = "seven", dtype: str = "f32") -> torch.Tensor:
+    """CPU buffer of n poisoned elements of `dtype` plus GUARD_COUNT trailing guards."""
+    buf = torch.empty(n + GUARD_COUNT, dtype=DTYPES[dtype])
     if poison == "seven":
         buf[:n] = POISON_VALUE
     elif poison == "nan":
-        buf[:n].view(torch.int32).fill_(NAN_POISON_BITS)
+        if dtype == "f32":
+            buf[:n].view(torch.int32).fill_(NAN_POISON_BITS)
+        else:
+            buf[:n] = float("nan")
     else:
         raise ValueError(poison)
     buf[n:] = GUARD_VALUE

@@ -24,6 +24,7 @@ BF16 = inputs.DTYPE_CODES["bf16"]
 def test_exports_every_declared_symbol(hip_lib):
     names = hip_lib.header_functions()
     assert set(names) == {"splitk_gemm_bt", "splitk_reduce", "splitk_gemm_bt_reduce",
+                          "splitk_reduce_typed", "splitk_gemm_bt_reduce_typed",
                           "splitk_status_str", "splitk_describe"}
     lib = hip_lib.load()
     for n in names:
@@ -115,6 +116,19 @@ class TestPointerChecksWithoutDevice:
         assert self.fused(hip_lib, C=P_PTR + p_bytes - 16) == ALIAS
         assert self.fused(hip_lib, C=A_PTR) == ALIAS
         assert hip_lib.raw_call("splitk_reduce", P_PTR, P_PTR + 1024, 2, 256, 1024, None) == ALIAS
+
+    def test_typed_output_checks(self, hip_lib):
+        call = lambda *a: hip_lib.raw_call("splitk_reduce_typed", *a)  # noqa: E731
+        assert call(P_PTR, C_PTR, 2, 256, 1024, 3, None) == DTYPE
+        assert call(P_PTR, C_PTR, 2, 256, 1024, -1, None) == DTYPE
+        assert call(None, C_PTR, 2, 256, 1024, 1, None) == NULL
+        assert call(P_PTR, C_PTR + 8, 2, 256, 1024, 2, None) == ALIGN
+        # A 16-bit C of M*N elements ends M*N*2 bytes after its start.
+        p_bytes = 2 * 256 * 1024 * 4
+        assert call(P_PTR, P_PTR + p_bytes - 16, 2, 256, 1024, 1, None) == ALIAS
+        fused = lambda *a: hip_lib.raw_call("splitk_gemm_bt_reduce_typed", *a)  # noqa: E731
+        assert fused(A_PTR, B_PTR, P_PTR, C_PTR, 256, 1024, 2048, 1024, 2, BF16, 5, None) == DTYPE
+        assert fused(A_PTR, B_PTR, P_PTR, A_PTR + 16, 256, 1024, 2048, 1024, 2, BF16, 1, None) == ALIAS
 
     def test_shape_errors_come_before_pointer_checks(self, hip_lib):
         assert self.gemm(hip_lib, A=A_PTR + 8, M=48) == SHAPE

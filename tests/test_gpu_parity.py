@@ -333,3 +333,67 @@ def test_reduce_alone_large_plane(sdg, S):
     ref, _, _ = oracle.slab_sum(ints.numpy())
     np.testing.assert_array_equal(got[: M * N].astype(np.float64), ref.ravel())
     assert np.all(got[M * N:].view(np.uint32) == GUARD_BITS)
+
+
+# ------------------------------------------------ typed final output
+# The F32 slab sum rounded to F16 or BF16 (nearest, ties to even); checked
+# with the pages' final-output tolerances for that type, and bit for bit
+# where every sum is exact (then the result is the oracle's encoding of the
+# exact value).
+
+GUARD16 = {"f16": np.float16(inputs.GUARD_VALUE).view(np.uint16),
+           "bf16": np.uint16(torch.tensor([inputs.GUARD_VALUE]).to(torch.bfloat16)
+                             .view(torch.int16).item() & 0xFFFF)}
+
+
+def _typed_run(sdg, a, b, kps, S, out):
+    dev = torch.device("cuda:0")
+    M, N = a.shape[0], b.shape[0]
+    P = torch.empty(S, M, N, device=dev)
+    cbuf = inputs.guarded_buffer(M * N, "nan", dtype=out).to(dev)
+    sdg.gemm_bt_reduce(a.to(dev), b.to(dev), P, cbuf[: M * N].view(M, N), kps, S)
+    torch.cuda.synchronize()
+    bits = inputs.stored_bits(cbuf.cpu())
+    assert np.all(bits[M * N:] == GUARD16[out]), "a trailing guard changed"
+    return bits[: M * N].reshape(M, N)
+
+
+@pytest.mark.parametrize("out", ["f16", "bf16"])
+@pytest.mark.parametrize("name", ["bf16_m96_n512_k2048_s4", "bf16_m256_n1024_k2048_s2",
+                                  "f16_m32_n512_k2080_s4", "f32_m32_n64_k64_s2"])
+def test_typed_output_parity(sdg, name, out):
+    w = inputs.WORKLOADS[name]
+    a, b = inputs.workload_operands(w)
+    bits = _typed_run(sdg, a, b, w.kps, w.splits, out)
+    RC, DC, _ = oracle.gemm_bt(_vals(a), _vals(b))
+    got = oracle.decode(bits, out)
+    assert not np.isnan(got).any()
+    err, _ = oracle.normalized_error(got, RC, DC)
+    _say(f"  typed {out} final err {err:.3e}")
+    assert err <= FINAL_TOL[out]
+
+
+@pytest.mark.parametrize("out", ["f16", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_typed_output_exact_inputs_bitwise(sdg, dtype, out):
+    M, N, K, kps, S = 96, 320, 480, 160, 3
+    a, b = inputs.exact_operands(M, N, K, dtype, seed=21)
+    bits = _typed_run(sdg, a, b, kps, S, out)
+    RC, _, _ = oracle.gemm_bt(_vals(a), _vals(b))
+    np.testing.assert_array_equal(bits, oracle.encode(RC, out))
+
+
+@pytest.mark.parametrize("out", ["f16", "bf16"])
+@pytest.mark.parametrize("S", [1, 3, 8, 11])
+@pytest.mark.parametrize("M,N", [(96, 320), (2048, 2048)])
+def test_typed_reduce_alone_bitwise(sdg, out, S, M, N):
+    dev = torch.device("cuda:0")
+    gen = torch.Generator().manual_seed(S + M)
+    slabs = torch.randint(-4000, 4000, (S, M, N), generator=gen).float().div_(64)
+    cbuf = inputs.guarded_buffer(M * N, "nan", dtype=out).to(dev)
+    sdg.reduce(slabs.to(dev), cbuf[: M * N].view(M, N), S)
+    torch.cuda.synchronize()
+    bits = inputs.stored_bits(cbuf.cpu())
+    ref, _, _ = oracle.slab_sum(slabs.numpy())   # exact: multiples of 1/64 well inside F32
+    np.testing.assert_array_equal(bits[: M * N], oracle.encode(ref, out).ravel())
+    assert np.all(bits[M * N:] == GUARD16[out])

@@ -372,3 +372,52 @@ def test_normalized_error_rules():
     assert e == math.inf and i == 1
     e, i = oracle.normalized_error(np.array([np.nan, 0.0, 2.0]), ref, den)
     assert e == math.inf and i == 0
+
+
+# ------------------------------------------------------------ encoding
+# The typed final output rounds the F32 sum to F16 or BF16, nearest with
+# ties to even.  oracle.encode is pinned by exhaustive round trips through
+# the (separately pinned) decoder, by hand-made ties, and by numpy's and
+# torch's own conversions.
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_encode_round_trips_every_16_bit_pattern(dt):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    vals = oracle.decode(bits, dt)
+    keep = ~np.isnan(vals)
+    np.testing.assert_array_equal(oracle.encode(vals[keep], dt), bits[keep])
+
+
+@pytest.mark.parametrize("dt,x,want", [
+    ("f16", 1 + 2.0**-11, 0x3C00),          # tie between 1 and 1+2^-10 -> even (1)
+    ("f16", 1 + 3 * 2.0**-11, 0x3C02),      # tie between 1+2^-10 and 1+2^-9 -> even
+    ("f16", 65520.0, 0x7C00),               # halfway above the largest finite -> inf
+    ("f16", 65519.0, 0x7BFF),
+    ("f16", 2.0**-25, 0x0000),              # tie between 0 and the smallest subnormal -> 0
+    ("f16", 3 * 2.0**-25, 0x0002),          # tie between 1 and 2 subnormal quanta -> 2
+    ("f16", -2.0**-14, 0x8400),
+    ("bf16", 1 + 2.0**-8, 0x3F80),          # tie -> even (1)
+    ("bf16", 1 + 3 * 2.0**-8, 0x3F82),
+    ("bf16", -3.0, 0xC040),
+])
+def test_encode_ties_and_edges(dt, x, want):
+    assert int(oracle.encode(np.array([x]), dt)[0]) == want
+
+
+def test_encode_matches_numpy_and_torch():
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal(200000) * 10.0 ** rng.integers(-9, 5, 200000)
+    with np.errstate(over="ignore"):
+        np.testing.assert_array_equal(oracle.encode(x, "f16"), x.astype(np.float16).view(np.uint16))
+    np.testing.assert_array_equal(oracle.encode(x, "f32"), x.astype(np.float32).view(np.uint32))
+    x32 = x.astype(np.float32).astype(np.float64)  # torch rounds via F32; compare where that is exact
+    want = torch.from_numpy(x32).float().to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(oracle.encode(x32, "bf16"), want)
+
+
+def test_truncating_encoder_is_caught():
+    """A plausible mistake (truncation instead of rounding) fails the tie pins."""
+    x = np.array([1 + 3 * 2.0**-11])
+    truncated = (x.astype(np.float32).view(np.uint32) >> 13).astype(np.uint16) - (0x1C000 >> 13)
+    assert int(truncated[0]) != int(oracle.encode(x, "f16")[0])

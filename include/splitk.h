@@ -68,7 +68,8 @@ typedef enum {
     SPLITK_ERR_ALIAS = 5,  /* an output overlaps an input or the other output       */
     SPLITK_ERR_ALIGN = 6,  /* a base pointer is not 16-byte aligned                 */
     SPLITK_ERR_RANGE = 7,  /* a buffer holds 2^31 elements or more                  */
-    SPLITK_ERR_LAUNCH = 8  /* the HIP runtime refused the launch                    */
+    SPLITK_ERR_LAUNCH = 8, /* the HIP runtime refused the launch                    */
+    SPLITK_ERR_WORKSPACE = 9 /* workspace smaller than the chosen geometry needs    */
 } splitk_status;
 
 /*
@@ -126,6 +127,44 @@ int splitk_reduce_typed(const float* partials, void* C, int64_t splits, int64_t 
 int splitk_gemm_bt_reduce_typed(const void* A, const void* B, float* partials, void* C, int64_t M,
                                 int64_t N, int64_t K, int64_t k_per_split, int64_t splits,
                                 int dtype, int out_dtype, void* stream);
+
+/*
+ * Automatic split count.  The pages time each shape at the split counts
+ * 1, 2, 4, 8 and 16 and keep the fastest (first page, "Measurement
+ * protocol"; second page, "Performance method").  This call makes that
+ * choice without running anything: it ranks the same candidates with a cost
+ * model of this library's kernels on one MI355X (the GEMM's workgroup rounds
+ * over 256 CUs and its HBM traffic, plus the accumulation pass) and returns
+ * the cheapest valid geometry.
+ *   k_per_split, splits  the chosen geometry (k_per_split a multiple of 32,
+ *                        of 64 for F16/BF16 where K allows).
+ *   workspace_elems      F32 elements splitk_gemm_bt_auto needs as workspace
+ *                        for it: splits*M*N, or 0 when one split writes an
+ *                        F32 C directly.
+ *   out_dtype            the splitk_dtype of C (an F16/BF16 C always needs
+ *                        the rounding pass, hence workspace).
+ * Host only; deterministic for given arguments.  Returns SPLITK_ERR_NULL for a
+ * NULL output pointer and otherwise the shape, dtype and range checks of
+ * splitk_gemm_bt.
+ */
+int splitk_choose_splits(int64_t M, int64_t N, int64_t K, int dtype, int out_dtype,
+                         int64_t* k_per_split, int64_t* splits, int64_t* workspace_elems);
+
+/*
+ * C = A * B^T with the geometry splitk_choose_splits picks.  With one split
+ * and an F32 C the GEMM writes C directly and no accumulation pass runs
+ * (the splits = 1 case of the pages' sampled grid); otherwise the slabs go
+ * to `workspace` and the pass (typed as out_dtype) writes C.
+ *   workspace        F32 device buffer of workspace_elems elements; may be
+ *                    NULL when the chosen geometry needs none.  Its contents
+ *                    are overwritten; it must not overlap A, B or C.
+ *   C                [M,N] of out_dtype, written in full.
+ * Returns SPLITK_ERR_WORKSPACE (nothing launched) when workspace_elems is
+ * below the need splitk_choose_splits reports, else as splitk_gemm_bt_reduce.
+ */
+int splitk_gemm_bt_auto(const void* A, const void* B, float* workspace, int64_t workspace_elems,
+                        void* C, int64_t M, int64_t N, int64_t K, int dtype, int out_dtype,
+                        void* stream);
 
 /* Static text for a status code ("unknown status" for anything else). */
 const char* splitk_status_str(int status);

@@ -8,8 +8,10 @@ over it (torch provides device memory and streams only).
 from ._lib import (  # noqa: F401
     DTYPE_CODE,
     SplitKError,
+    choose_splits,
     describe,
     gemm_bt,
+    gemm_bt_auto,
     gemm_bt_reduce,
     header_functions,
     library_built,

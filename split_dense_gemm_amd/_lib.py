@@ -23,7 +23,7 @@ DTYPE_CODE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 _STATUS_NAMES = {
     0: "SPLITK_OK", 1: "SPLITK_ERR_NULL", 2: "SPLITK_ERR_DTYPE", 3: "SPLITK_ERR_SHAPE",
     4: "SPLITK_ERR_SPLIT", 5: "SPLITK_ERR_ALIAS", 6: "SPLITK_ERR_ALIGN", 7: "SPLITK_ERR_RANGE",
-    8: "SPLITK_ERR_LAUNCH",
+    8: "SPLITK_ERR_LAUNCH", 9: "SPLITK_ERR_WORKSPACE",
 }
 
 _lib = None
@@ -64,6 +64,11 @@ def load():
     lib.splitk_reduce_typed.restype = I
     lib.splitk_gemm_bt_reduce_typed.argtypes = [P, P, P, P, I64, I64, I64, I64, I64, I, I, P]
     lib.splitk_gemm_bt_reduce_typed.restype = I
+    PI64 = ctypes.POINTER(I64)
+    lib.splitk_choose_splits.argtypes = [I64, I64, I64, I, I, PI64, PI64, PI64]
+    lib.splitk_choose_splits.restype = I
+    lib.splitk_gemm_bt_auto.argtypes = [P, P, P, I64, P, I64, I64, I64, I, I, P]
+    lib.splitk_gemm_bt_auto.restype = I
     lib.splitk_status_str.argtypes = [I]
     lib.splitk_status_str.restype = ctypes.c_char_p
     lib.splitk_describe.argtypes = [I64, I64, I64, I64, I64, I, ctypes.c_char_p, I64]
@@ -174,9 +179,41 @@ def gemm_bt_reduce(A: torch.Tensor, B: torch.Tensor, partials: torch.Tensor, C: 
     return C
 
 
+def _code(dtype) -> int:
+    return DTYPE_CODE[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+
+
+def choose_splits(M: int, N: int, K: int, dtype, out_dtype=torch.float32):
+    """(k_per_split, splits, workspace_elems) the library picks for C = A*B^T
+    with an `out_dtype` C (see splitk.h); nothing is launched."""
+    kps, s, ws = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    _check(load().splitk_choose_splits(M, N, K, _code(dtype), _code(out_dtype), ctypes.byref(kps),
+                                       ctypes.byref(s), ctypes.byref(ws)))
+    return kps.value, s.value, ws.value
+
+
+def gemm_bt_auto(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, workspace=None,
+                 stream=None) -> torch.Tensor:
+    """C = A * B^T with the split count the library chooses (see splitk.h).
+    `workspace` is a float32 device tensor of at least the elements
+    choose_splits() reports, or None when it reports none."""
+    M, N, K, dt = _operands(A, B)
+    out = _out(C, M * N)
+    if workspace is None:
+        wp, wn = None, 0
+    else:
+        _dev(workspace, "workspace")
+        if workspace.dtype != torch.float32:
+            raise ValueError("workspace must be float32")
+        wp, wn = workspace.data_ptr(), workspace.numel()
+    _check(load().splitk_gemm_bt_auto(A.data_ptr(), B.data_ptr(), wp, wn, C.data_ptr(), M, N, K, dt,
+                                      out, _stream(stream)))
+    return C
+
+
 def describe(M: int, N: int, K: int, k_per_split: int, splits: int, dtype) -> str:
     """The GEMM kernel configuration the library picks for this problem."""
-    code = DTYPE_CODE[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    code = _code(dtype)
     buf = ctypes.create_string_buffer(128)
     _check(load().splitk_describe(M, N, K, k_per_split, splits, code, buf, len(buf)))
     return buf.value.decode()

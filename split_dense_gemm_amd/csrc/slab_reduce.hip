@@ -69,12 +69,22 @@ __global__ __launch_bounds__(kBlock) void slab_reduce_kernel(const f32x4* __rest
             }
         }
     } else {
-        // Any other split count: ascending-s loop.
+        // Any other split count: slabs in batches of eight whose loads are
+        // all issued before their adds, still summed in ascending s.
+        constexpr int kBatch = 8;
         for (int it = 0; it < ITEMS; ++it) {
             const int64_t g = g0 + it * stride;
             if (g >= plane4) break;
             f32x4 acc = P[g];
-            for (int s = 1; s < splits; ++s) acc += P[(int64_t)s * plane4 + g];
+            int s = 1;
+            for (; s + kBatch <= splits; s += kBatch) {
+                f32x4 v[kBatch];
+#pragma unroll
+                for (int j = 0; j < kBatch; ++j) v[j] = P[(int64_t)(s + j) * plane4 + g];
+#pragma unroll
+                for (int j = 0; j < kBatch; ++j) acc += v[j];
+            }
+            for (; s < splits; ++s) acc += P[(int64_t)s * plane4 + g];
             store4<OT>(C, g, acc);
         }
     }

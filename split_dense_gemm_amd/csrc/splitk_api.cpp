@@ -77,6 +77,22 @@ int check_reduce(const float* P, const void* C, int64_t splits, int64_t M, int64
     return SPLITK_OK;
 }
 
+// Shape and type checks of the automatic-split entry points (no split
+// geometry is given, so only the operands' own domain is checked).
+int check_auto_shape(int64_t M, int64_t N, int64_t K, int dtype, int out_dtype) {
+    if (!valid_dtype(dtype) || !valid_dtype(out_dtype)) return SPLITK_ERR_DTYPE;
+    if (M <= 0 || N <= 0 || K <= 0 || M % 32 || K % 32 || N % 64) return SPLITK_ERR_SHAPE;
+    if (M >= kMaxElems || N >= kMaxElems || K >= kMaxElems) return SPLITK_ERR_RANGE;
+    if (M * K >= kMaxElems || N * K >= kMaxElems || M * N >= kMaxElems) return SPLITK_ERR_RANGE;
+    return SPLITK_OK;
+}
+
+// F32 elements of workspace the automatic path needs: none when one split
+// writes an F32 C directly, else the slabs.
+int64_t auto_workspace(int64_t splits, int64_t M, int64_t N, int out_dtype) {
+    return (splits == 1 && out_dtype == SPLITK_F32) ? 0 : splits * M * N;
+}
+
 }  // namespace
 
 extern "C" {
@@ -95,6 +111,8 @@ const char* splitk_status_str(int status) {
         case SPLITK_ERR_ALIGN: return "a pointer is not 16-byte aligned";
         case SPLITK_ERR_RANGE: return "a buffer holds 2^31 elements or more";
         case SPLITK_ERR_LAUNCH: return "kernel launch failed";
+        case SPLITK_ERR_WORKSPACE:
+            return "workspace smaller than the chosen split geometry needs (see splitk_choose_splits)";
         default: return "unknown status";
     }
 }
@@ -146,6 +164,46 @@ int splitk_gemm_bt_reduce(const void* A, const void* B, float* partials, float* 
                           void* stream) {
     return splitk_gemm_bt_reduce_typed(A, B, partials, C, M, N, K, k_per_split, splits, dtype,
                                        SPLITK_F32, stream);
+}
+
+int splitk_choose_splits(int64_t M, int64_t N, int64_t K, int dtype, int out_dtype,
+                         int64_t* k_per_split, int64_t* splits, int64_t* workspace_elems) {
+    if (!k_per_split || !splits || !workspace_elems) return SPLITK_ERR_NULL;
+    int st = check_auto_shape(M, N, K, dtype, out_dtype);
+    if (st != SPLITK_OK) return st;
+    int64_t kps = 0, s = 0;
+    if (!splitk::choose_split(dtype, out_dtype, M, N, K, &kps, &s)) return SPLITK_ERR_RANGE;
+    *k_per_split = kps;
+    *splits = s;
+    *workspace_elems = auto_workspace(s, M, N, out_dtype);
+    return SPLITK_OK;
+}
+
+int splitk_gemm_bt_auto(const void* A, const void* B, float* workspace, int64_t workspace_elems,
+                        void* C, int64_t M, int64_t N, int64_t K, int dtype, int out_dtype,
+                        void* stream) {
+    if (!A || !B || !C) return SPLITK_ERR_NULL;
+    int64_t kps = 0, s = 0, need = 0;
+    int st = splitk_choose_splits(M, N, K, dtype, out_dtype, &kps, &s, &need);
+    if (st != SPLITK_OK) return st;
+    if (workspace_elems < need) return SPLITK_ERR_WORKSPACE;
+    const splitk::GemmPlan plan = splitk::plan_gemm(dtype, M, N, K, kps, s);
+    if (need == 0) {
+        // One split, F32 output: the GEMM's single slab is C itself.
+        st = check_gemm_pointers(A, B, (const float*)C, nullptr, M, N, K, 1, dtype, 0);
+        if (st != SPLITK_OK) return st;
+        hipError_t e = splitk::launch_gemm_bt(plan, A, B, (float*)C, M, N, K, kps, 1, dtype,
+                                              (hipStream_t)stream);
+        return e == hipSuccess ? SPLITK_OK : SPLITK_ERR_LAUNCH;
+    }
+    if (!workspace) return SPLITK_ERR_NULL;
+    st = check_gemm_pointers(A, B, workspace, C, M, N, K, s, dtype, element_bytes(out_dtype));
+    if (st != SPLITK_OK) return st;
+    hipError_t e = splitk::launch_gemm_bt(plan, A, B, workspace, M, N, K, kps, s, dtype,
+                                          (hipStream_t)stream);
+    if (e != hipSuccess) return SPLITK_ERR_LAUNCH;
+    e = splitk::launch_slab_reduce(workspace, C, s, M, N, out_dtype, (hipStream_t)stream);
+    return e == hipSuccess ? SPLITK_OK : SPLITK_ERR_LAUNCH;
 }
 
 int splitk_describe(int64_t M, int64_t N, int64_t K, int64_t k_per_split, int64_t splits, int dtype,

@@ -40,4 +40,15 @@ hipError_t launch_gemm_bt(const GemmPlan& plan, const void* A, const void* B, fl
 hipError_t launch_slab_reduce(const float* partials, void* C, int64_t splits, int64_t M, int64_t N,
                               int out_dtype, hipStream_t stream);
 
+// Split-count choice (split_choice.cpp).  Modelled microseconds of one GEMM
+// launch and of one accumulation pass on MI355X.
+double gemm_cost_us(const GemmPlan& p, int dtype, int64_t M, int64_t N, int64_t K, int64_t kps,
+                    int64_t splits);
+double reduce_cost_us(int64_t splits, int64_t M, int64_t N, int out_dtype);
+// k_per_split for `splits` even slices of K (0 if no valid geometry exists).
+int64_t split_length(int dtype, int64_t K, int64_t splits);
+// The candidate with the lowest modelled time; false if none is valid.
+bool choose_split(int dtype, int out_dtype, int64_t M, int64_t N, int64_t K, int64_t* kps,
+                  int64_t* splits);
+
 }  // namespace splitk

@@ -16,7 +16,7 @@ import pytest
 from conftest import gpu_available
 from split_dense_gemm_amd import inputs
 
-OK, NULL, DTYPE, SHAPE, SPLIT, ALIAS, ALIGN, RANGE = 0, 1, 2, 3, 4, 5, 6, 7
+OK, NULL, DTYPE, SHAPE, SPLIT, ALIAS, ALIGN, RANGE, LAUNCH, WORKSPACE = range(10)
 
 BF16 = inputs.DTYPE_CODES["bf16"]
 
@@ -25,6 +25,7 @@ def test_exports_every_declared_symbol(hip_lib):
     names = hip_lib.header_functions()
     assert set(names) == {"splitk_gemm_bt", "splitk_reduce", "splitk_gemm_bt_reduce",
                           "splitk_reduce_typed", "splitk_gemm_bt_reduce_typed",
+                          "splitk_choose_splits", "splitk_gemm_bt_auto",
                           "splitk_status_str", "splitk_describe"}
     lib = hip_lib.load()
     for n in names:
@@ -33,8 +34,8 @@ def test_exports_every_declared_symbol(hip_lib):
 
 def test_status_strings(hip_lib):
     lib = hip_lib.load()
-    texts = [lib.splitk_status_str(s).decode() for s in range(9)]
-    assert texts[0] == "ok" and len(set(texts)) == 9
+    texts = [lib.splitk_status_str(s).decode() for s in range(10)]
+    assert texts[0] == "ok" and len(set(texts)) == 10 and "unknown status" not in texts
     assert lib.splitk_status_str(99).decode() == "unknown status"
 
 
@@ -130,6 +131,27 @@ class TestPointerChecksWithoutDevice:
         assert fused(A_PTR, B_PTR, P_PTR, C_PTR, 256, 1024, 2048, 1024, 2, BF16, 5, None) == DTYPE
         assert fused(A_PTR, B_PTR, P_PTR, A_PTR + 16, 256, 1024, 2048, 1024, 2, BF16, 1, None) == ALIAS
 
+    def test_auto_checks(self, hip_lib):
+        def auto(A=A_PTR, B=B_PTR, W=P_PTR, wn=1 << 30, C=C_PTR, M=256, N=1024, K=2048, dt=BF16, ot=0):
+            return hip_lib.raw_call("splitk_gemm_bt_auto", A, B, W, wn, C, M, N, K, dt, ot, None)
+        assert auto(C=None) == NULL
+        assert auto(A=None) == NULL
+        assert auto(ot=7) == DTYPE
+        assert auto(M=48) == SHAPE
+        # Workspace: too small is its own status; NULL with a need is NULL.
+        kps, s, need = hip_lib.choose_splits(32, 512, 16384, BF16)
+        assert s > 1 and need == s * 32 * 512
+        assert auto(M=32, N=512, K=16384, wn=need - 1) == WORKSPACE
+        assert auto(M=32, N=512, K=16384, W=None, wn=need) == NULL
+        assert auto(M=32, N=512, K=16384, wn=need, W=P_PTR + 4) == ALIGN
+        assert auto(M=32, N=512, K=16384, wn=need, W=A_PTR) == ALIAS
+        assert auto(M=32, N=512, K=16384, wn=need, C=P_PTR + 16) == ALIAS
+        # One split with an F32 C needs no workspace; C must not overlap A or B.
+        kps, s, need = hip_lib.choose_splits(4096, 8192, 1024, BF16)
+        assert (s, need) == (1, 0)
+        assert auto(M=4096, N=8192, K=1024, W=None, wn=0, C=A_PTR) == ALIAS
+        assert auto(M=4096, N=8192, K=1024, W=None, wn=0, C=C_PTR + 8) == ALIGN
+
     def test_shape_errors_come_before_pointer_checks(self, hip_lib):
         assert self.gemm(hip_lib, A=A_PTR + 8, M=48) == SHAPE
         assert self.gemm(hip_lib, P=A_PTR, S=3) == SPLIT
@@ -145,3 +167,50 @@ def test_binding_rejects_host_tensors(hip_lib):
     p = torch.zeros(2, 32, 64)
     with pytest.raises(ValueError):
         hip_lib.gemm_bt(a, b, p, 32, 2)
+
+
+# ------------------------------------------------ automatic split count
+# Host logic only: the choice among the sampled split counts of "Aligned
+# shared rows for pipelined NAX on CUDA", section "Measurement protocol".
+
+CHOICE_SHAPES = [(m, n, k) for m in (32, 96, 256, 1024, 4096) for n in (64, 512, 4096, 8192)
+                 for k in (32, 96, 1024, 2080, 16384)]
+
+
+@pytest.mark.parametrize("dt", [0, 1, 2])
+@pytest.mark.parametrize("ot", [0, 1, 2])
+def test_choice_is_a_valid_geometry(hip_lib, dt, ot):
+    for M, N, K in CHOICE_SHAPES:
+        kps, s, need = hip_lib.choose_splits(M, N, K, dt, ot)
+        assert s in (1, 2, 4, 8, 16), (M, N, K, s)
+        assert kps % 32 == 0 and (s - 1) * kps < K <= s * kps, (M, N, K, kps, s)
+        assert need == (0 if (s == 1 and ot == 0) else s * M * N)
+        if dt != 0 and K % 64 == 0 and s > 1:
+            assert kps % 64 == 0, "16-bit splits should hold whole 128-byte chunks"
+        assert hip_lib.describe(M, N, K, kps, s, dt)  # the GEMM accepts it
+        assert hip_lib.choose_splits(M, N, K, dt, ot) == (kps, s, need)  # deterministic
+
+
+def test_choice_follows_the_measured_extremes(hip_lib):
+    # Decided by wide margins in MI355X measurements of the chain
+    # (e.g. 82 us with one split against 200 us with two for the first).
+    assert hip_lib.choose_splits(4096, 8192, 1024, BF16)[1] == 1
+    assert hip_lib.choose_splits(2048, 8192, 8192, BF16)[1] == 1
+    assert hip_lib.choose_splits(32, 512, 16384, BF16)[1] >= 4
+    assert hip_lib.choose_splits(512, 8192, 16384, BF16)[1] >= 2
+    assert hip_lib.choose_splits(256, 8192, 8192, BF16)[1] >= 2
+    # Short K leaves nothing to split.
+    assert hip_lib.choose_splits(256, 1024, 32, BF16)[1] == 1
+
+
+@pytest.mark.parametrize("args,status", [
+    ((48, 512, 1024, BF16, 0), SHAPE), ((32, 96, 1024, BF16, 0), SHAPE),
+    ((32, 512, 1000, BF16, 0), SHAPE), ((32, 512, 0, BF16, 0), SHAPE),
+    ((32, 512, 1024, 3, 0), DTYPE), ((32, 512, 1024, BF16, 9), DTYPE),
+    ((1 << 16, 64, 1 << 15, BF16, 0), RANGE),
+])
+def test_choice_checks(hip_lib, args, status):
+    out = [ctypes.c_int64() for _ in range(3)]
+    assert hip_lib.load().splitk_choose_splits(*args, *[ctypes.byref(o) for o in out]) == status
+    assert hip_lib.load().splitk_choose_splits(32, 512, 1024, BF16, 0, None, ctypes.byref(out[1]),
+                                               ctypes.byref(out[2])) == NULL

@@ -166,6 +166,29 @@ int splitk_gemm_bt_auto(const void* A, const void* B, float* workspace, int64_t 
                         void* C, int64_t M, int64_t N, int64_t K, int dtype, int out_dtype,
                         void* stream);
 
+/*
+ * The same split-K GEMM with B stored [K,N] instead of [N,K]: row k of B holds
+ * B[k,0..N-1] contiguously (n-major weights).  The pages prepare weights in
+ * both orders ("Wider consecutive-weight NAX GEMM", section "Performance
+ * method"); the operation is unchanged:
+ *   partials[s,i,j] = sum_{k in slice s} A[i,k] * B[k,j].
+ *   B   [K,N] elements of `dtype`, read only, resident weights.
+ * Every other argument, the shape domain, the checks and the statuses are
+ * those of splitk_gemm_bt (B still spans N*K elements).
+ */
+int splitk_gemm_bn(const void* A, const void* B, float* partials, int64_t M, int64_t N, int64_t K,
+                   int64_t k_per_split, int64_t splits, int dtype, void* stream);
+
+/*
+ * splitk_gemm_bn then the accumulation pass on the same stream, C [M,N] of
+ * out_dtype (F32, or F16/BF16 rounded to nearest even as in
+ * splitk_reduce_typed).  All arguments are checked before either kernel is
+ * enqueued.
+ */
+int splitk_gemm_bn_reduce(const void* A, const void* B, float* partials, void* C, int64_t M,
+                          int64_t N, int64_t K, int64_t k_per_split, int64_t splits, int dtype,
+                          int out_dtype, void* stream);
+
 /* Static text for a status code ("unknown status" for anything else). */
 const char* splitk_status_str(int status);
 
@@ -178,6 +201,10 @@ const char* splitk_status_str(int status);
  */
 int splitk_describe(int64_t M, int64_t N, int64_t K, int64_t k_per_split, int64_t splits,
                     int dtype, char* buf, int64_t len);
+
+/* As splitk_describe, for splitk_gemm_bn (B stored [K,N]). */
+int splitk_describe_bn(int64_t M, int64_t N, int64_t K, int64_t k_per_split, int64_t splits,
+                       int dtype, char* buf, int64_t len);
 
 #ifdef __cplusplus
 }

@@ -10,6 +10,9 @@ from ._lib import (  # noqa: F401
     SplitKError,
     choose_splits,
     describe,
+    describe_bn,
+    gemm_bn,
+    gemm_bn_reduce,
     gemm_bt,
     gemm_bt_auto,
     gemm_bt_reduce,

@@ -69,6 +69,12 @@ def load():
     lib.splitk_choose_splits.restype = I
     lib.splitk_gemm_bt_auto.argtypes = [P, P, P, I64, P, I64, I64, I64, I, I, P]
     lib.splitk_gemm_bt_auto.restype = I
+    lib.splitk_gemm_bn.argtypes = [P, P, P, I64, I64, I64, I64, I64, I, P]
+    lib.splitk_gemm_bn.restype = I
+    lib.splitk_gemm_bn_reduce.argtypes = [P, P, P, P, I64, I64, I64, I64, I64, I, I, P]
+    lib.splitk_gemm_bn_reduce.restype = I
+    lib.splitk_describe_bn.argtypes = [I64, I64, I64, I64, I64, I, ctypes.c_char_p, I64]
+    lib.splitk_describe_bn.restype = I
     lib.splitk_status_str.argtypes = [I]
     lib.splitk_status_str.restype = ctypes.c_char_p
     lib.splitk_describe.argtypes = [I64, I64, I64, I64, I64, I, ctypes.c_char_p, I64]
@@ -115,6 +121,19 @@ def _operands(A: torch.Tensor, B: torch.Tensor):
     if A.shape[1] != B.shape[1]:
         raise ValueError(f"A is {tuple(A.shape)} and B is {tuple(B.shape)}: K differs")
     return A.shape[0], B.shape[0], A.shape[1], DTYPE_CODE[A.dtype]
+
+
+def _operands_kn(A: torch.Tensor, B: torch.Tensor):
+    """A [M,K] and B stored [K,N]."""
+    _dev(A, "A")
+    _dev(B, "B")
+    if A.dim() != 2 or B.dim() != 2:
+        raise ValueError("A must be [M,K] and B [K,N]")
+    if A.dtype != B.dtype or A.dtype not in DTYPE_CODE:
+        raise ValueError(f"A and B must share one of float32/float16/bfloat16, got {A.dtype}, {B.dtype}")
+    if A.shape[1] != B.shape[0]:
+        raise ValueError(f"A is {tuple(A.shape)} and B is {tuple(B.shape)}: K differs")
+    return A.shape[0], B.shape[1], A.shape[1], DTYPE_CODE[A.dtype]
 
 
 def _f32_out(t: torch.Tensor, name: str, numel: int):
@@ -209,6 +228,36 @@ def gemm_bt_auto(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, workspace=No
     _check(load().splitk_gemm_bt_auto(A.data_ptr(), B.data_ptr(), wp, wn, C.data_ptr(), M, N, K, dt,
                                       out, _stream(stream)))
     return C
+
+
+def gemm_bn(A: torch.Tensor, B: torch.Tensor, partials: torch.Tensor, k_per_split: int, splits: int,
+            stream=None) -> torch.Tensor:
+    """partials[s,i,j] = sum over split s's k range of A[i,k]*B[k,j], with B
+    stored [K,N] (see splitk.h)."""
+    M, N, K, dt = _operands_kn(A, B)
+    _f32_out(partials, "partials", splits * M * N)
+    _check(load().splitk_gemm_bn(A.data_ptr(), B.data_ptr(), partials.data_ptr(), M, N, K,
+                                 int(k_per_split), int(splits), dt, _stream(stream)))
+    return partials
+
+
+def gemm_bn_reduce(A: torch.Tensor, B: torch.Tensor, partials: torch.Tensor, C: torch.Tensor,
+                   k_per_split: int, splits: int, stream=None) -> torch.Tensor:
+    """gemm_bn then the slab sum into C (float32, float16 or bfloat16)."""
+    M, N, K, dt = _operands_kn(A, B)
+    _f32_out(partials, "partials", splits * M * N)
+    out = _out(C, M * N)
+    _check(load().splitk_gemm_bn_reduce(A.data_ptr(), B.data_ptr(), partials.data_ptr(), C.data_ptr(),
+                                        M, N, K, int(k_per_split), int(splits), dt, out,
+                                        _stream(stream)))
+    return C
+
+
+def describe_bn(M: int, N: int, K: int, k_per_split: int, splits: int, dtype) -> str:
+    """The kernel configuration gemm_bn picks for this problem."""
+    buf = ctypes.create_string_buffer(128)
+    _check(load().splitk_describe_bn(M, N, K, k_per_split, splits, _code(dtype), buf, len(buf)))
+    return buf.value.decode()
 
 
 def describe(M: int, N: int, K: int, k_per_split: int, splits: int, dtype) -> str:

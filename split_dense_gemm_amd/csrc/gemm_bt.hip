@@ -104,7 +104,66 @@ __device__ inline int xcd_logical_id(int b, int n) {
 // consecutive rows all slots differ.
 __device__ inline int slot_of(int r, int p) { return p ^ (r & 7) ^ ((r >> 3) & 1); }
 
-template <int DT, int BM, int BN, int W, int D>
+// ---------------------------------------------------------------------------
+// B stored as [K,N] (n contiguous) instead of [N,K].
+//
+// A chunk of B is then CK k-rows of the tile's BN columns: CK*BN*ES bytes,
+// the same 128 bytes per column as in the [N,K] case, held in LDS as the
+// dense [CK][BN] tile cut into 128-byte units (unit u = bytes 128u..128u+127
+// of the tile).  Granule p (16 bytes) of unit u sits in slot p ^ (u & 2);
+// the flip of granule bit 1 on every other pair of units keeps the
+// transposing fragment reads below off each other's banks.
+__device__ inline int kn_slot(int u, int p) { return p ^ (u & 2); }
+
+// LDS byte offset, inside the B tile, of byte b of the dense [CK][BN] tile.
+__device__ inline int kn_lds(int b) {
+    const int u = b >> 7;
+    return (u << 7) | (kn_slot(u, (b >> 4) & 7) << 4) | (b & 15);
+}
+
+// Global byte offset, from the first element of the split's first k-row in
+// the tile's columns, of the 16 bytes that fill slot j of unit u.
+template <int ES, int BN>
+__device__ inline size_t kn_src(int u, int j, size_t row_bytes_b) {
+    const int byte = u * kChunkBytes + kn_slot(u, j) * 16;
+    return (size_t)(byte / (BN * ES)) * row_bytes_b + (size_t)(byte % (BN * ES));
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// MFMA B fragment of step q for the 32 columns of block nb from a [K,N]
+// tile.  16-bit types: lane l needs B[16q + 8(l/32) + t][32nb + l%32] for
+// t = 0..7, the same k slots as the A fragment (piece 2q + l/32 of its row).
+// ds_read_tr16_b64 hands lane i of each group of 16 lanes element i%4 of the
+// 8 bytes addressed by lane 4j + i/4 of the group, as its element j.  So a
+// lane addresses 4 consecutive columns of one k-row: group g covers columns
+// 16(g%2) .. +15 for k-rows 16q + 8(g/2) + j (j = 0..3), and a second read
+// 4 k-rows further down gives t = 4..7.
+template <int DT, int BN>
+__device__ inline u32x4 kn_frag(const uint8_t* tile, int q, int nb, int lane) {
+    if constexpr (DT == 0) {
+        // F32: lane l needs B[8q + 4(l/32) + e][32nb + l%32] for e = 0..3.
+        u32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int krow = 8 * q + 4 * (lane >> 5) + e;
+            v[e] = *(const uint32_t*)(tile + kn_lds(krow * BN * 4 + (nb * 32 + (lane & 31)) * 4));
+        }
+        return v;
+    } else {
+        const int g = lane >> 4;
+        const int krow = 16 * q + 8 * (g >> 1) + ((lane >> 2) & 3);
+        const int colb = (nb * 32 + 16 * (g & 1) + 4 * (lane & 3)) * 2;
+        typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + kn_lds(krow * BN * 2 + colb)));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + kn_lds((krow + 4) * BN * 2 + colb)));
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+        return u32x4{l2.x, l2.y, h2.x, h2.y};
+    }
+}
+
+template <int DT, int BM, int BN, int W, int D, int BL>
 __global__ __launch_bounds__(W * 64) void gemm_bt_wavek(const uint8_t* __restrict__ A,
                                                         const uint8_t* __restrict__ B,
                                                         float* __restrict__ P, int M, int N, int K,
@@ -145,16 +204,24 @@ __global__ __launch_bounds__(W * 64) void gemm_bt_wavek(const uint8_t* __restric
     // writes LDS slot lane%8 of it, so each load instruction of the wave reads
     // eight whole 128-byte row segments and writes 1 KiB of LDS contiguously.
     const size_t row_bytes = (size_t)K * ES;
+    const size_t row_bytes_b = (size_t)N * ES;  // [K,N] layout: one k-row of B
     const int lrow = lane >> 3, lslot = lane & 7;
     const uint8_t* src[LOADS];
     int piece[LOADS];
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
         const int row = 8 * i + lrow;
-        src[i] = row < BM ? A + (size_t)(mt * BM + row) * row_bytes
-                          : B + (size_t)(nt * BN + row - BM) * row_bytes;
-        src[i] += (size_t)k0 * ES;
         piece[i] = slot_of(row, lslot);  // the global piece that lands in slot lslot
+        if (BL == 1 && i >= BM / 8) {
+            // Unit row - BM of the [CK][BN] tile; its slot lslot.
+            src[i] = B + (size_t)k0 * row_bytes_b + (size_t)nt * BN * ES +
+                     kn_src<ES, BN>(row - BM, lslot, row_bytes_b);
+            piece[i] = 0;
+        } else {
+            src[i] = row < BM ? A + (size_t)(mt * BM + row) * row_bytes
+                              : B + (size_t)(nt * BN + row - BM) * row_bytes;
+            src[i] += (size_t)k0 * ES;
+        }
     }
     uint8_t* lds = smem + wave * ROWS * kChunkBytes;
 
@@ -177,11 +244,20 @@ __global__ __launch_bounds__(W * 64) void gemm_bt_wavek(const uint8_t* __restric
 
     auto load = [&](int c, u32x4 (&t)[LOADS]) {
         // In a half chunk the lanes meant for pieces 4..7 re-read pieces 0..3
-        // (in bounds); those slots are never consumed.
-        const int mask = half_chunk(c) ? 3 : 7;
+        // (in bounds); those slots are never consumed.  With B as [K,N] the
+        // units holding k-rows CK/2.. re-read the rows CK/2 above instead.
+        const bool half = half_chunk(c);
+        const int mask = half ? 3 : 7;
         const size_t off = (size_t)c * kChunkBytes;
 #pragma unroll
-        for (int i = 0; i < LOADS; ++i) t[i] = *(const u32x4*)(src[i] + off + (piece[i] & mask) * 16);
+        for (int i = 0; i < LOADS; ++i) {
+            if (BL == 1 && i >= BM / 8) {
+                const size_t up = (half && i >= (BM + BN / 2) / 8) ? (size_t)(CK / 2) * row_bytes_b : 0;
+                t[i] = *(const u32x4*)(src[i] + (size_t)c * CK * row_bytes_b - up);
+            } else {
+                t[i] = *(const u32x4*)(src[i] + off + (piece[i] & mask) * 16);
+            }
+        }
     };
     auto compute = [&](int c, u32x4 (&t)[LOADS]) {
         // Stage the chunk in this wave's LDS buffer (row 8*i + lane/8, slot lane%8).
@@ -201,8 +277,12 @@ __global__ __launch_bounds__(W * 64) void gemm_bt_wavek(const uint8_t* __restric
             }
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
-                const int row = BM + nb * 32 + r;
-                fb[nb] = *(const u32x4*)(lds + row * kChunkBytes + slot_of(row, 2 * q + h) * 16);
+                if (BL == 1) {
+                    fb[nb] = kn_frag<DT, BN>(lds + BM * kChunkBytes, q, nb, lane);
+                } else {
+                    const int row = BM + nb * 32 + r;
+                    fb[nb] = *(const u32x4*)(lds + row * kChunkBytes + slot_of(row, 2 * q + h) * 16);
+                }
             }
 #pragma unroll
             for (int e = 0; e < Op::kStepsPerPiece; ++e)
@@ -279,7 +359,7 @@ __device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_b
 // fills slot j of row r fetches piece slot_of(r, j)).  Accumulators are
 // stored straight to the partial slab: for each accumulator register the 32
 // lanes of a half-wave write 32 consecutive floats of one row.
-template <int DT, int BM, int BN, int WM, int WN, int NBUF>
+template <int DT, int BM, int BN, int WM, int WN, int NBUF, int BL>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_bt_tiled(const uint8_t* __restrict__ A,
                                                               const uint8_t* __restrict__ B,
                                                               float* __restrict__ P, int M, int N,
@@ -297,6 +377,11 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bt_tiled(const uint8_t* __r
     constexpr int GM = 4;                     // row tiles per group of the tile order
     static_assert(ROWS % (8 * NW) == 0 && BM % 8 == 0, "staging split");
     static_assert((NBUF - 2) * DPW < 64, "vmcnt range");
+    // DMA instruction i fills rows 8*(i*NW + wave) ..: for these sizes the
+    // A rows, the B rows and (for B as [K,N]) the B units holding the second
+    // half of a chunk's k-rows begin at the same i in every wave.
+    constexpr int IA = BM / 8 / NW, IH = (BM + BN / 2) / 8 / NW;
+    static_assert((BM / 8) % NW == 0 && ((BM + BN / 2) / 8) % NW == 0, "row split per wave");
     __shared__ __attribute__((aligned(16))) uint8_t smem[NBUF * BUF];
 
     // Tile order: split major; inside a split, groups of GM row tiles sweep
@@ -328,28 +413,46 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bt_tiled(const uint8_t* __r
     // DMA instruction i of this wave fills rows 8*g .. 8*g+7 (g = i*NW + wave)
     // of a buffer; this lane fills slot lane%8 of row 8*g + lane/8.
     const size_t row_bytes = (size_t)K * ES;
+    const size_t row_bytes_b = (size_t)N * ES;  // [K,N] layout: one k-row of B
     const uint8_t* src[DPW];
     int piece[DPW];
 #pragma unroll
     for (int i = 0; i < DPW; ++i) {
         const int row = 8 * (i * NW + wave) + (lane >> 3);
-        src[i] = (row < BM ? A + (size_t)(mt * BM + row) * row_bytes
-                           : B + (size_t)(nt * BN + row - BM) * row_bytes) +
-                 (size_t)k0 * ES;
         piece[i] = slot_of(row, lane & 7);
+        if (BL == 1 && i >= IA) {
+            src[i] = B + (size_t)k0 * row_bytes_b + (size_t)nt * BN * ES +
+                     kn_src<ES, BN>(row - BM, lane & 7, row_bytes_b);
+            piece[i] = 0;
+        } else {
+            src[i] = (row < BM ? A + (size_t)(mt * BM + row) * row_bytes
+                               : B + (size_t)(nt * BN + row - BM) * row_bytes) +
+                     (size_t)k0 * ES;
+        }
     }
     // Chunk c into ring slot c % NBUF.  In a half chunk the lanes meant for
     // pieces 4..7 re-read pieces 0..3 (in bounds); those copies are finite
     // and meet zero A fragments in compute().
     auto dma = [&](int c) {
         uint8_t* buf = smem + (c % NBUF) * BUF;
-        const int mask = half_chunk(c) ? 3 : 7;
+        const bool half = half_chunk(c);
+        const int mask = half ? 3 : 7;
         const size_t off = (size_t)c * kChunkBytes;
 #pragma unroll
-        for (int i = 0; i < DPW; ++i)
-            __builtin_amdgcn_global_load_lds((const void*)(src[i] + off + (piece[i] & mask) * 16),
+        for (int i = 0; i < DPW; ++i) {
+            const uint8_t* g;
+            if (BL == 1 && i >= IA) {
+                // B as [K,N]: in a half chunk the second half of the k-rows
+                // re-reads the first half (in bounds, never consumed).
+                const size_t up = (half && i >= IH) ? (size_t)(CK / 2) * row_bytes_b : 0;
+                g = src[i] + (size_t)c * CK * row_bytes_b - up;
+            } else {
+                g = src[i] + off + (piece[i] & mask) * 16;
+            }
+            __builtin_amdgcn_global_load_lds((const void*)g,
                                              (__attribute__((address_space(3))) void*)(buf + (i * NW + wave) * 1024),
                                              16, 0, 0);
+        }
     };
 
     f32x16 acc[MB][NB];
@@ -372,8 +475,12 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bt_tiled(const uint8_t* __r
             }
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
-                const int row = BM + wn * TN + nb * 32 + r;
-                fb[nb] = *(const u32x4*)(lds + row * kChunkBytes + slot_of(row, 2 * q + h) * 16);
+                if (BL == 1) {
+                    fb[nb] = kn_frag<DT, BN>(lds + BM * kChunkBytes, q, wn * (TN / 32) + nb, lane);
+                } else {
+                    const int row = BM + wn * TN + nb * 32 + r;
+                    fb[nb] = *(const u32x4*)(lds + row * kChunkBytes + slot_of(row, 2 * q + h) * 16);
+                }
             }
 #pragma unroll
             for (int e = 0; e < Op::kStepsPerPiece; ++e)
@@ -416,7 +523,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bt_tiled(const uint8_t* __r
                 out[(size_t)(mb * 32 + 8 * (i >> 2) + 4 * h + (i & 3)) * N + nb * 32 + r] = acc[mb][nb][i];
 }
 
-template <int DT, int BM, int BN, int WM, int WN, int NBUF>
+template <int DT, int BM, int BN, int WM, int WN, int NBUF, int BL>
 hipError_t launch_tiled(const void* A, const void* B, float* P, int64_t M, int64_t N, int64_t K,
                         int64_t kps, int64_t splits, hipStream_t stream) {
     const int tiles_m = (int)(M / BM), tiles_n = (int)(N / BN);
@@ -426,7 +533,7 @@ hipError_t launch_tiled(const void* A, const void* B, float* P, int64_t M, int64
     const uint8_t* b = (const uint8_t*)B;
     int m = (int)M, n = (int)N, k = (int)K, kp = (int)kps;
     void* args[] = {&a, &b, &P, &m, &n, &k, &kp, (void*)&tiles_m, (void*)&tiles_n};
-    return hipLaunchKernel((const void*)&gemm_bt_tiled<DT, BM, BN, WM, WN, NBUF>, grid, block, args,
+    return hipLaunchKernel((const void*)&gemm_bt_tiled<DT, BM, BN, WM, WN, NBUF, BL>, grid, block, args,
                            0, stream);
 }
 
@@ -630,7 +737,7 @@ hipError_t launch_wavek_dma(const void* A, const void* B, float* P, int64_t M, i
                            0, stream);
 }
 
-template <int DT, int BM, int BN, int W, int D>
+template <int DT, int BM, int BN, int W, int D, int BL>
 hipError_t launch_wavek(const void* A, const void* B, float* P, int64_t M, int64_t N, int64_t K,
                         int64_t kps, int64_t splits, hipStream_t stream) {
     const int tiles_m = (int)(M / BM), tiles_n = (int)(N / BN);
@@ -640,7 +747,7 @@ hipError_t launch_wavek(const void* A, const void* B, float* P, int64_t M, int64
     const uint8_t* b = (const uint8_t*)B;
     int m = (int)M, n = (int)N, k = (int)K, kp = (int)kps;
     void* args[] = {&a, &b, &P, &m, &n, &k, &kp, (void*)&tiles_m, (void*)&tiles_n};
-    return hipLaunchKernel((const void*)&gemm_bt_wavek<DT, BM, BN, W, D>, grid, block, args, 0,
+    return hipLaunchKernel((const void*)&gemm_bt_wavek<DT, BM, BN, W, D, BL>, grid, block, args, 0,
                            stream);
 }
 
@@ -666,13 +773,48 @@ hipError_t launch_wavek(const void* A, const void* B, float* P, int64_t M, int64
     X(64, 64, 4, 2)             \
     X(64, 64, 4, 4)
 
+// Instantiated configurations for B stored as [K,N]: the register-staged
+// skinny kernel and the large-tile kernel (the DMA-tail skinny kernel
+// transposes 32 B rows at a time, which has no counterpart when B's rows are
+// k-rows).
+#define SPLITK_KN_WAVEK_CONFIGS(X) \
+    X(32, 32, 8, 1)                \
+    X(32, 32, 8, 2)                \
+    X(32, 64, 8, 1)                \
+    X(32, 64, 8, 2)
+
+#define SPLITK_KN_TILED_CONFIGS(X) \
+    X(256, 256, 2, 2)              \
+    X(256, 128, 2, 2)
+
 template <int DT>
-hipError_t launch_dtype(const GemmPlan& p, const void* A, const void* B, float* P, int64_t M,
-                        int64_t N, int64_t K, int64_t kps, int64_t splits, hipStream_t st) {
+hipError_t launch_dtype_kn(const GemmPlan& p, const void* A, const void* B, float* P, int64_t M,
+                           int64_t N, int64_t K, int64_t kps, int64_t splits, hipStream_t st) {
     if (p.kind == kWaveK) {
 #define X(cbm, cbn, cw, cd)                                                    \
     if (p.bm == cbm && p.bn == cbn && p.waves == cw && p.stages == cd)        \
-        return launch_wavek<DT, cbm, cbn, cw, cd>(A, B, P, M, N, K, kps, splits, st);
+        return launch_wavek<DT, cbm, cbn, cw, cd, 1>(A, B, P, M, N, K, kps, splits, st);
+        SPLITK_KN_WAVEK_CONFIGS(X)
+#undef X
+    }
+    if (p.kind == kTiled) {
+#define X(cbm, cbn, cwm, cwn)                                                     \
+    if (p.bm == cbm && p.bn == cbn && p.waves == cwm * cwn && p.stages == cwm)    \
+        return launch_tiled<DT, cbm, cbn, cwm, cwn, tiled_nbuf<cbm, cbn>(), 1>(A, B, P, M, N, K, kps, splits, st);
+        SPLITK_KN_TILED_CONFIGS(X)
+#undef X
+    }
+    return hipErrorInvalidConfiguration;
+}
+
+template <int DT>
+hipError_t launch_dtype(const GemmPlan& p, const void* A, const void* B, float* P, int64_t M,
+                        int64_t N, int64_t K, int64_t kps, int64_t splits, hipStream_t st) {
+    if (p.layout == kLayoutKN) return launch_dtype_kn<DT>(p, A, B, P, M, N, K, kps, splits, st);
+    if (p.kind == kWaveK) {
+#define X(cbm, cbn, cw, cd)                                                    \
+    if (p.bm == cbm && p.bn == cbn && p.waves == cw && p.stages == cd)        \
+        return launch_wavek<DT, cbm, cbn, cw, cd, 0>(A, B, P, M, N, K, kps, splits, st);
         SPLITK_WAVEK_CONFIGS(X)
 #undef X
     }
@@ -686,7 +828,7 @@ hipError_t launch_dtype(const GemmPlan& p, const void* A, const void* B, float* 
     if (p.kind == kTiled) {
 #define X(cbm, cbn, cwm, cwn)                                                     \
     if (p.bm == cbm && p.bn == cbn && p.waves == cwm * cwn && p.stages == cwm)    \
-        return launch_tiled<DT, cbm, cbn, cwm, cwn, tiled_nbuf<cbm, cbn>()>(A, B, P, M, N, K, kps, splits, st);
+        return launch_tiled<DT, cbm, cbn, cwm, cwn, tiled_nbuf<cbm, cbn>(), 0>(A, B, P, M, N, K, kps, splits, st);
         SPLITK_TILED_CONFIGS(X)
 #undef X
     }
@@ -701,9 +843,13 @@ bool wavekdma_config_exists(int bm, int bn, int w, int r) {
     return false;
 }
 
-bool wavek_config_exists(int bm, int bn, int w, int d) {
+bool wavek_config_exists(int layout, int bm, int bn, int w, int d) {
 #define X(cbm, cbn, cw, cd) \
     if (bm == cbm && bn == cbn && w == cw && d == cd) return true;
+    if (layout == kLayoutKN) {
+        SPLITK_KN_WAVEK_CONFIGS(X)
+        return false;
+    }
     SPLITK_WAVEK_CONFIGS(X)
 #undef X
     return false;
@@ -711,9 +857,13 @@ bool wavek_config_exists(int bm, int bn, int w, int d) {
 
 }  // namespace
 
-bool tiled_config_exists(int bm, int bn, int wm, int wn) {
+bool tiled_config_exists(int layout, int bm, int bn, int wm, int wn) {
 #define X(cbm, cbn, cwm, cwn) \
     if (bm == cbm && bn == cbn && wm == cwm && wn == cwn) return true;
+    if (layout == kLayoutKN) {
+        SPLITK_KN_TILED_CONFIGS(X)
+        return false;
+    }
     SPLITK_TILED_CONFIGS(X)
 #undef X
     return false;
@@ -724,34 +874,38 @@ bool tiled_config_exists(int bm, int bn, int wm, int wn) {
 // configuration wherever its tile divides the problem.  Read on every call
 // (a getenv is negligible next to a launch); unset or unknown values leave
 // the automatic choice in place.
-static bool forced_plan(int* kind, int* v) {
+static bool forced_plan(int layout, int* kind, int* v) {
     const char* e = getenv("SPLITK_PLAN");
     char name[16] = {0};  // "wavek", "wavekdma" or "tiled"
     if (!e || sscanf(e, "%15[a-z],%d,%d,%d,%d", name, &v[0], &v[1], &v[2], &v[3]) != 5) return false;
-    if (!strcmp(name, "wavek") && wavek_config_exists(v[0], v[1], v[2], v[3])) { *kind = kWaveK; return true; }
-    if (!strcmp(name, "wavekdma") && wavekdma_config_exists(v[0], v[1], v[2], v[3])) { *kind = kWaveKDma; return true; }
-    if (!strcmp(name, "tiled") && tiled_config_exists(v[0], v[1], v[2], v[3])) { *kind = kTiled; return true; }
+    if (!strcmp(name, "wavek") && wavek_config_exists(layout, v[0], v[1], v[2], v[3])) { *kind = kWaveK; return true; }
+    if (!strcmp(name, "wavekdma") && layout == kLayoutNK && wavekdma_config_exists(v[0], v[1], v[2], v[3])) {
+        *kind = kWaveKDma;
+        return true;
+    }
+    if (!strcmp(name, "tiled") && tiled_config_exists(layout, v[0], v[1], v[2], v[3])) { *kind = kTiled; return true; }
     return false;
 }
 
-GemmPlan plan_gemm(int dtype, int64_t M, int64_t N, int64_t K, int64_t kps, int64_t splits) {
+GemmPlan plan_gemm(int dtype, int64_t M, int64_t N, int64_t K, int64_t kps, int64_t splits,
+                   int layout) {
     (void)K;
     const int64_t es = dtype == 0 ? 4 : 2;
     const int64_t ck = 128 / es;  // elements per 128-byte chunk
     const int64_t max_chunks = (kps + ck - 1) / ck;  // chunks of the longest split
     int fk, f[4];
-    if (forced_plan(&fk, f) && M % f[0] == 0 && N % f[1] == 0 &&
+    if (forced_plan(layout, &fk, f) && M % f[0] == 0 && N % f[1] == 0 &&
         (fk != kWaveKDma || max_chunks <= (int64_t)f[2] * (f[3] + 1))) {
         const int64_t wg = (M / f[0]) * (N / f[1]) * splits;
-        if (fk == kTiled) return GemmPlan{kTiled, f[0], f[1], f[2] * f[3], f[2], wg, f[2] * f[3] * 64};
-        return GemmPlan{fk, f[0], f[1], f[2], f[3], wg, f[2] * 64};
+        if (fk == kTiled) return GemmPlan{kTiled, f[0], f[1], f[2] * f[3], f[2], wg, f[2] * f[3] * 64, layout};
+        return GemmPlan{fk, f[0], f[1], f[2], f[3], wg, f[2] * 64, layout};
     }
     // Large problems: 256x256 tiles (2x2 waves) when there is at least one
     // per CU, else 256x128; these read the least L2 data per flop.
     if (M % 256 == 0 && N % 256 == 0 && (M / 256) * (N / 256) * splits >= 256)
-        return GemmPlan{kTiled, 256, 256, 4, 2, (M / 256) * (N / 256) * splits, 256};
+        return GemmPlan{kTiled, 256, 256, 4, 2, (M / 256) * (N / 256) * splits, 256, layout};
     if (M % 256 == 0 && N % 128 == 0 && (M / 256) * (N / 128) * splits >= 256)
-        return GemmPlan{kTiled, 256, 128, 4, 2, (M / 256) * (N / 128) * splits, 256};
+        return GemmPlan{kTiled, 256, 128, 4, 2, (M / 256) * (N / 128) * splits, 256, layout};
     // Skinny problems.  Tile: the one that moves the fewest bytes through
     // the busiest CU.  Each workgroup streams (BM + BN) rows of its split,
     // and workgroups beyond the 256 CUs queue behind the first round.
@@ -773,11 +927,11 @@ GemmPlan plan_gemm(int dtype, int64_t M, int64_t N, int64_t K, int64_t kps, int6
     const int64_t wg = (M / bm) * (N / bn) * splits;
     // Each wave's last chunk by LDS DMA whenever a wave has at most two.
     const int64_t per_wave = (chunks + w - 1) / w;
-    if (per_wave <= 2 && wavekdma_config_exists(bm, bn, w, (int)per_wave - 1))
-        return GemmPlan{kWaveKDma, bm, bn, w, (int)per_wave - 1, wg, w * 64};
+    if (layout == kLayoutNK && per_wave <= 2 && wavekdma_config_exists(bm, bn, w, (int)per_wave - 1))
+        return GemmPlan{kWaveKDma, bm, bn, w, (int)per_wave - 1, wg, w * 64, layout};
     int d = per_wave >= 2 ? 2 : 1;
-    while (d > 1 && !wavek_config_exists(bm, bn, w, d)) d /= 2;
-    return GemmPlan{kWaveK, bm, bn, w, d, wg, w * 64};
+    while (d > 1 && !wavek_config_exists(layout, bm, bn, w, d)) d /= 2;
+    return GemmPlan{kWaveK, bm, bn, w, d, wg, w * 64, layout};
 }
 
 hipError_t launch_gemm_bt(const GemmPlan& plan, const void* A, const void* B, float* partials,

@@ -93,6 +93,39 @@ int64_t auto_workspace(int64_t splits, int64_t M, int64_t N, int out_dtype) {
     return (splits == 1 && out_dtype == SPLITK_F32) ? 0 : splits * M * N;
 }
 
+// GEMM (and, when C is given, the accumulation pass) for either layout of B.
+int gemm_entry(int layout, const void* A, const void* B, float* P, void* C, int64_t M, int64_t N,
+               int64_t K, int64_t kps, int64_t splits, int dtype, int out_dtype, void* stream) {
+    if (!A || !B || !P) return SPLITK_ERR_NULL;
+    int st = check_gemm_shape(M, N, K, kps, splits, dtype);
+    if (st != SPLITK_OK) return st;
+    if (C && !valid_dtype(out_dtype)) return SPLITK_ERR_DTYPE;
+    st = check_gemm_pointers(A, B, P, C, M, N, K, splits, dtype, C ? element_bytes(out_dtype) : 0);
+    if (st != SPLITK_OK) return st;
+    const splitk::GemmPlan plan = splitk::plan_gemm(dtype, M, N, K, kps, splits, layout);
+    hipError_t e = splitk::launch_gemm_bt(plan, A, B, P, M, N, K, kps, splits, dtype, (hipStream_t)stream);
+    if (e != hipSuccess) return SPLITK_ERR_LAUNCH;
+    if (C) e = splitk::launch_slab_reduce(P, C, splits, M, N, out_dtype, (hipStream_t)stream);
+    return e == hipSuccess ? SPLITK_OK : SPLITK_ERR_LAUNCH;
+}
+
+int describe_plan(int layout, int64_t M, int64_t N, int64_t K, int64_t k_per_split, int64_t splits,
+                  int dtype, char* buf, int64_t len) {
+    int st = check_gemm_shape(M, N, K, k_per_split, splits, dtype);
+    if (st != SPLITK_OK) return st;
+    const splitk::GemmPlan p = splitk::plan_gemm(dtype, M, N, K, k_per_split, splits, layout);
+    if (buf && len > 0) {
+        if (p.kind == splitk::kTiled)
+            snprintf(buf, (size_t)len, "tiled bm%d bn%d waves%dx%d block%d grid%lld", p.bm, p.bn,
+                     p.stages, p.waves / p.stages, p.block, (long long)p.grid);
+        else
+            snprintf(buf, (size_t)len, "%s bm%d bn%d waves%d stages%d block%d grid%lld",
+                     p.kind == splitk::kWaveKDma ? "wavekdma" : "wavek", p.bm, p.bn, p.waves, p.stages,
+                     p.block, (long long)p.grid);
+    }
+    return SPLITK_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -208,19 +241,26 @@ int splitk_gemm_bt_auto(const void* A, const void* B, float* workspace, int64_t 
 
 int splitk_describe(int64_t M, int64_t N, int64_t K, int64_t k_per_split, int64_t splits, int dtype,
                     char* buf, int64_t len) {
-    int st = check_gemm_shape(M, N, K, k_per_split, splits, dtype);
-    if (st != SPLITK_OK) return st;
-    const splitk::GemmPlan p = splitk::plan_gemm(dtype, M, N, K, k_per_split, splits);
-    if (buf && len > 0) {
-        if (p.kind == splitk::kTiled)
-            snprintf(buf, (size_t)len, "tiled bm%d bn%d waves%dx%d block%d grid%lld", p.bm, p.bn,
-                     p.stages, p.waves / p.stages, p.block, (long long)p.grid);
-        else
-            snprintf(buf, (size_t)len, "%s bm%d bn%d waves%d stages%d block%d grid%lld",
-                     p.kind == splitk::kWaveKDma ? "wavekdma" : "wavek", p.bm, p.bn, p.waves, p.stages,
-                     p.block, (long long)p.grid);
-    }
-    return SPLITK_OK;
+    return describe_plan(splitk::kLayoutNK, M, N, K, k_per_split, splits, dtype, buf, len);
+}
+
+int splitk_gemm_bn(const void* A, const void* B, float* partials, int64_t M, int64_t N, int64_t K,
+                   int64_t k_per_split, int64_t splits, int dtype, void* stream) {
+    return gemm_entry(splitk::kLayoutKN, A, B, partials, nullptr, M, N, K, k_per_split, splits, dtype,
+                      SPLITK_F32, stream);
+}
+
+int splitk_gemm_bn_reduce(const void* A, const void* B, float* partials, void* C, int64_t M,
+                          int64_t N, int64_t K, int64_t k_per_split, int64_t splits, int dtype,
+                          int out_dtype, void* stream) {
+    if (!C) return SPLITK_ERR_NULL;
+    return gemm_entry(splitk::kLayoutKN, A, B, partials, C, M, N, K, k_per_split, splits, dtype,
+                      out_dtype, stream);
+}
+
+int splitk_describe_bn(int64_t M, int64_t N, int64_t K, int64_t k_per_split, int64_t splits,
+                       int dtype, char* buf, int64_t len) {
+    return describe_plan(splitk::kLayoutKN, M, N, K, k_per_split, splits, dtype, buf, len);
 }
 
 }  // extern "C"

@@ -22,15 +22,20 @@ enum GemmKind : int {
     kWaveKDma = 2,
 };
 
+// Storage of B: [N,K] (each row k-contiguous) or [K,N] (each row n-contiguous).
+enum BLayout : int { kLayoutNK = 0, kLayoutKN = 1 };
+
 struct GemmPlan {
     int kind;
     int bm, bn, waves, stages;  // tiled kernels: stages = waves along M
     int64_t grid;  // workgroups
     int block;     // threads per workgroup
+    int layout;    // BLayout of B
 };
 
 // Chooses the kernel configuration for a validated problem.
-GemmPlan plan_gemm(int dtype, int64_t M, int64_t N, int64_t K, int64_t kps, int64_t splits);
+GemmPlan plan_gemm(int dtype, int64_t M, int64_t N, int64_t K, int64_t kps, int64_t splits,
+                   int layout = kLayoutNK);
 
 hipError_t launch_gemm_bt(const GemmPlan& plan, const void* A, const void* B, float* partials,
                           int64_t M, int64_t N, int64_t K, int64_t kps, int64_t splits, int dtype,

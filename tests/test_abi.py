@@ -26,6 +26,7 @@ def test_exports_every_declared_symbol(hip_lib):
     assert set(names) == {"splitk_gemm_bt", "splitk_reduce", "splitk_gemm_bt_reduce",
                           "splitk_reduce_typed", "splitk_gemm_bt_reduce_typed",
                           "splitk_choose_splits", "splitk_gemm_bt_auto",
+                          "splitk_gemm_bn", "splitk_gemm_bn_reduce", "splitk_describe_bn",
                           "splitk_status_str", "splitk_describe"}
     lib = hip_lib.load()
     for n in names:
@@ -214,3 +215,31 @@ def test_choice_checks(hip_lib, args, status):
     assert hip_lib.load().splitk_choose_splits(*args, *[ctypes.byref(o) for o in out]) == status
     assert hip_lib.load().splitk_choose_splits(32, 512, 1024, BF16, 0, None, ctypes.byref(out[1]),
                                                ctypes.byref(out[2])) == NULL
+
+
+# ------------------------------------------------ B stored [K,N]
+
+@pytest.mark.parametrize("args,status", SHAPE_CASES)
+def test_describe_bn_checks_shape_and_split(hip_lib, args, status):
+    buf = ctypes.create_string_buffer(128)
+    assert hip_lib.load().splitk_describe_bn(*args, buf, len(buf)) == status
+
+
+def test_bn_plans_never_use_the_dma_tail_kernel(hip_lib):
+    for M, N, K, kps, S in [(32, 512, 2048, 512, 4), (256, 1024, 2048, 1024, 2),
+                            (2048, 4096, 4096, 512, 8), (96, 512, 2048, 512, 4)]:
+        text = hip_lib.describe_bn(M, N, K, kps, S, BF16)
+        assert text.startswith(("wavek ", "tiled ")), text
+
+
+@pytest.mark.skipif(gpu_available(), reason="made-up pointers are only passed where no GPU exists")
+def test_bn_pointer_checks_without_device(hip_lib):
+    bn = lambda *a: hip_lib.raw_call("splitk_gemm_bn", *a)  # noqa: E731
+    assert bn(A_PTR, None, P_PTR, 256, 1024, 2048, 1024, 2, BF16, None) == NULL
+    assert bn(A_PTR, B_PTR + 4, P_PTR, 256, 1024, 2048, 1024, 2, BF16, None) == ALIGN
+    assert bn(A_PTR, B_PTR, B_PTR + 64, 256, 1024, 2048, 1024, 2, BF16, None) == ALIAS
+    assert bn(A_PTR, B_PTR, P_PTR, 256, 1024, 2048, 1024, 3, BF16, None) == SPLIT
+    red = lambda *a: hip_lib.raw_call("splitk_gemm_bn_reduce", *a)  # noqa: E731
+    assert red(A_PTR, B_PTR, P_PTR, None, 256, 1024, 2048, 1024, 2, BF16, 0, None) == NULL
+    assert red(A_PTR, B_PTR, P_PTR, C_PTR, 256, 1024, 2048, 1024, 2, BF16, 4, None) == DTYPE
+    assert red(A_PTR, B_PTR, P_PTR, A_PTR, 256, 1024, 2048, 1024, 2, BF16, 0, None) == ALIAS

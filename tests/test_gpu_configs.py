@@ -8,7 +8,9 @@ Acceptance as in test_gpu_parity.py (tolerances of "Aligned shared rows for
 pipelined NAX on CUDA", section "Contract and correctness").
 
 The configuration lists are read from the kernel source so that a newly
-instantiated configuration is tested without editing this file.
+instantiated configuration is tested without editing this file.  The
+configurations instantiated for B stored [K,N] run through splitk_gemm_bn
+with the same operands, B handed over as the transpose of the [N,K] array.
 """
 from __future__ import annotations
 
@@ -37,6 +39,8 @@ def _configs(macro):
 WAVEK = _configs("SPLITK_WAVEK_CONFIGS")
 WAVEKDMA = _configs("SPLITK_WAVEKDMA_CONFIGS")
 TILED = _configs("SPLITK_TILED_CONFIGS")
+KN_WAVEK = _configs("SPLITK_KN_WAVEK_CONFIGS")
+KN_TILED = _configs("SPLITK_KN_TILED_CONFIGS")
 
 
 def _shape(kind, cfg):
@@ -56,42 +60,53 @@ def _shape(kind, cfg):
     return 2 * bm, 2 * bn, 2 * 608 + 32, 608, 3
 
 
-CASES = ([("wavek", c) for c in WAVEK] + [("wavekdma", c) for c in WAVEKDMA] +
-         [("tiled", c) for c in TILED])
+CASES = ([("nk", "wavek", c) for c in WAVEK] + [("nk", "wavekdma", c) for c in WAVEKDMA] +
+         [("nk", "tiled", c) for c in TILED] + [("kn", "wavek", c) for c in KN_WAVEK] +
+         [("kn", "tiled", c) for c in KN_TILED])
 
 
 def _plan_text(kind, cfg):
     return f"{kind},{cfg[0]},{cfg[1]},{cfg[2]},{cfg[3]}"
 
 
+def _case_id(case):
+    layout, kind, cfg = case
+    return f"{layout}:{_plan_text(kind, cfg)}"
+
+
 @pytest.fixture
 def forced(request):
-    kind, cfg = request.param
+    layout, kind, cfg = request.param
     old = os.environ.get("SPLITK_PLAN")
     os.environ["SPLITK_PLAN"] = _plan_text(kind, cfg)
-    yield kind, cfg
+    yield layout, kind, cfg
     if old is None:
         os.environ.pop("SPLITK_PLAN", None)
     else:
         os.environ["SPLITK_PLAN"] = old
 
 
-@pytest.mark.parametrize("forced", CASES, indirect=True, ids=lambda c: _plan_text(*c))
+@pytest.mark.parametrize("forced", CASES, indirect=True, ids=_case_id)
 def test_override_is_honoured(hip_lib, forced):
-    kind, cfg = forced
+    layout, kind, cfg = forced
     M, N, K, kps, S = _shape(kind, cfg)
-    text = hip_lib.describe(M, N, K, kps, S, 2)
+    describe = hip_lib.describe if layout == "nk" else hip_lib.describe_bn
+    text = describe(M, N, K, kps, S, 2)
     assert text.startswith(kind) and f"bm{cfg[0]} bn{cfg[1]}" in text, text
 
 
 @pytest.mark.gpu
 @pytest.mark.skipif(not gpu_available(), reason="no GPU")
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
-@pytest.mark.parametrize("forced", CASES, indirect=True, ids=lambda c: _plan_text(*c))
+@pytest.mark.parametrize("forced", CASES, indirect=True, ids=_case_id)
 def test_config_parity(hip_lib, forced, dtype):
-    kind, cfg = forced
+    layout, kind, cfg = forced
     M, N, K, kps, S = _shape(kind, cfg)
-    print(f"case {_plan_text(kind, cfg)} {dtype} M{M} N{N} K{K} kps{kps} S{S}", flush=True)
+    print(f"case {layout}:{_plan_text(kind, cfg)} {dtype} M{M} N{N} K{K} kps{kps} S{S}", flush=True)
+    # B as the library receives it: [N,K], or its transpose stored [K,N].
+    stored = (lambda t: t) if layout == "nk" else (lambda t: t.T.contiguous())
+    gemm_reduce = hip_lib.gemm_bt_reduce if layout == "nk" else hip_lib.gemm_bn_reduce
+    gemm = hip_lib.gemm_bt if layout == "nk" else hip_lib.gemm_bn
     dev = torch.device("cuda:0")
     a, b = inputs.make_operands(M, N, K, dtype, seed=cfg[0] + cfg[1] + cfg[2] + cfg[3],
                                 zero_first_row=True, scale_last_row=True)
@@ -101,8 +116,8 @@ def test_config_parity(hip_lib, forced, dtype):
     RC, DC, _ = oracle.gemm_bt(a64, b64)
     pbuf = inputs.guarded_buffer(S * M * N, "nan").to(dev)
     cbuf = inputs.guarded_buffer(M * N, "nan").to(dev)
-    hip_lib.gemm_bt_reduce(a.to(dev), b.to(dev), pbuf[: S * M * N].view(S, M, N),
-                           cbuf[: M * N].view(M, N), kps, S)
+    gemm_reduce(a.to(dev), stored(b).to(dev), pbuf[: S * M * N].view(S, M, N),
+                cbuf[: M * N].view(M, N), kps, S)
     torch.cuda.synchronize()
     p, c = pbuf.cpu().numpy(), cbuf.cpu().numpy()
     guard = np.float32(inputs.GUARD_VALUE).view(np.uint32)
@@ -119,6 +134,6 @@ def test_config_parity(hip_lib, forced, dtype):
     eb64 = oracle.decode(inputs.stored_bits(eb), dtype)
     EP, _, _ = oracle.splitk_partials(ea64, eb64, kps, S)
     P = torch.empty(S, M, N, device=dev)
-    hip_lib.gemm_bt(ea.to(dev), eb.to(dev), P, kps, S)
+    gemm(ea.to(dev), stored(eb).to(dev), P, kps, S)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(P.cpu().numpy().astype(np.float64), EP)

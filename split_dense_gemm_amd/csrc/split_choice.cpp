@@ -8,16 +8,21 @@
 // model of this library's own kernels on one 256-CU MI355X, so that no timing
 // runs at call time:
 //
-//   GEMM    rounds * (a + b * staged MB per workgroup) + t0, floored by the
-//           HBM time of its unique traffic, where rounds = workgroups /
-//           (256 CUs * workgroups resident per CU), rounded up;
+//   GEMM    t0 + rounds * (a + b * MB staged per wave + c * MB staged per
+//           workgroup), floored by the HBM time of its unique traffic, where
+//           rounds = workgroups / (256 CUs * workgroups resident per CU),
+//           rounded up.  In the skinny kernels a wave's own chunk count sets
+//           the critical path (the waves of a workgroup share the split's
+//           chunks); the large-tile kernels have no per-wave term;
 //   reduce  r0 + bytes moved / bandwidth (+ one more load round past eight
 //           slabs); absent when one split writes C directly.
 //
-// The coefficients are least-squares fits to measured MI355X times of every
-// (kernel family, element size) over 200 BF16 and 45 F32 shapes
-// (M 32..4096, N 512..8192, K 1024..16384).  Candidates that are not powers of two
-// (3, 6, 12) never won in those measurements and are not considered.
+// The coefficients are least-squares fits (relative error) to measured
+// MI355X times of each (kernel family, element size): 480 BF16 shapes (M
+// 32..4096, N 512..8192, K 1024..16384, including a dense grid of the small
+// shapes M 32..320, N 512..1536, K 1024..6144) and 45 F32 shapes, each at
+// all five split counts.  Candidates that are not powers of two (3, 6, 12)
+// never won in those measurements and are not considered.
 #include <math.h>
 #include <stdint.h>
 
@@ -29,19 +34,21 @@ namespace {
 constexpr double kCus = 256.0;
 constexpr double kHbmBytesPerUs = 5.5e6;   // sustained HBM3E rate, bytes per microsecond
 constexpr double kHbmFloorUs = 1.0;
-constexpr double kReduceBaseUs = 1.7;      // launch and one load round trip
-constexpr double kReduceUsPerMB = 0.156;   // about 6.4 TB/s
-constexpr double kReduceExtraRoundUs = 1.8;  // more than eight slabs: a second batch of loads
+constexpr double kReduceBaseUs = 1.95;       // launch gap and one load round trip
+constexpr double kReduceUsPerMB = 0.157;      // about 6.4 TB/s
+constexpr double kReduceExtraRoundUs = 2.29;  // more than eight slabs: a second batch of loads
 
 struct Coef {
-    double t0, a, b;  // microseconds; b per MB staged by one workgroup
+    double t0, a;  // microseconds
+    double b;      // per MB staged by one wave (skinny kernels)
+    double c;      // per MB staged by one workgroup
 };
 
 // [element size 2 or 4][family]: skinny with DMA tail, skinny, tiled 256x128, tiled 256x256.
-constexpr Coef kCoef16[4] = {{0.57, 2.07, 10.65}, {0.04, 2.49, 11.84}, {3.90, 3.90, 22.60},
-                             {0.91, 10.67, 28.71}};
-constexpr Coef kCoef32[4] = {{0.20, 2.39, 23.72}, {-2.39, 4.52, 23.00}, {3.85, 3.85, 87.00},
-                             {1.64, 10.39, 122.15}};
+constexpr Coef kCoef16[4] = {{0.701, 1.510, 62.80, 5.154}, {-0.275, 2.723, 2.126, 11.14},
+                             {3.897, 3.897, 0.0, 22.61}, {0.912, 10.67, 0.0, 28.71}};
+constexpr Coef kCoef32[4] = {{0.543, 1.120, 140.1, 14.27}, {-2.394, 4.521, 2.831, 22.65},
+                             {3.854, 3.854, 0.0, 87.00}, {1.636, 10.39, 0.0, 122.1}};
 
 // Workgroups of one configuration resident on a CU at once, from each
 // kernel's LDS use (160 KiB per CU) and VGPR use (512 per lane per SIMD).
@@ -69,9 +76,13 @@ double gemm_cost_us(const GemmPlan& p, int dtype, int64_t M, int64_t N, int64_t 
                     int64_t splits) {
     const int64_t es = dtype == 0 ? 4 : 2;
     const double rounds = ceil((double)p.grid / (kCus * resident_per_cu(p)));
-    const double staged_mb = (double)(p.bm + p.bn) * (double)kps * (double)es / 1e6;
+    // Staged bytes: 128 per row of the BM + BN tile rows per chunk; a wave of
+    // a skinny workgroup handles every waves-th chunk of the split.
+    const int64_t chunks = (kps * es + 127) / 128;
+    const double chunk_mb = (double)(p.bm + p.bn) * 128.0 / 1e6;
+    const double per_wave = p.kind == kTiled ? 0.0 : (double)((chunks + p.waves - 1) / p.waves) * chunk_mb;
     const Coef& c = coef_of(p, es);
-    const double t = c.t0 + rounds * (c.a + c.b * staged_mb);
+    const double t = c.t0 + rounds * (c.a + c.b * per_wave + c.c * (double)chunks * chunk_mb);
     const double hbm = ((double)(M + N) * (double)K * es + (double)splits * M * N * 4) / kHbmBytesPerUs;
     return fmax(t, kHbmFloorUs + hbm);
 }

@@ -21,7 +21,9 @@
  *   splitk_gemm_bt_reduce: the two above, back to back on one stream.
  *
  * Shape domain (same sections): M, K and k_per_split are positive multiples
- * of 32 and N is a positive multiple of 64.  Inputs have exactly the stated
+ * of 32.  The pages also require N to be a multiple of 64; this library
+ * accepts any positive N (the last column tile is narrowed: B rows past N are
+ * never read and output columns past N never written).  Inputs have exactly the stated
  * extents -- the library never reads past A[M*K] or B[N*K] and never writes
  * outside partials[splits*M*N] or C[M*N] -- and outputs are separate storage
  * that aliases nothing else.
@@ -61,8 +63,8 @@ typedef enum {
     SPLITK_OK = 0,
     SPLITK_ERR_NULL = 1,   /* a required pointer is NULL                            */
     SPLITK_ERR_DTYPE = 2,  /* dtype is not one of splitk_dtype                      */
-    SPLITK_ERR_SHAPE = 3,  /* M, K, k_per_split not positive multiples of 32, or N  */
-                           /* not a positive multiple of 64                         */
+    SPLITK_ERR_SHAPE = 3,  /* M, K, k_per_split not positive multiples of 32, N not */
+                           /* positive (not a multiple of 8 for splitk_gemm_bn)     */
     SPLITK_ERR_SPLIT = 4,  /* splits < 1, a slice starting at or past K, or the     */
                            /* slices not covering K                                 */
     SPLITK_ERR_ALIAS = 5,  /* an output overlaps an input or the other output       */
@@ -91,7 +93,7 @@ int splitk_gemm_bt(const void* A, const void* B, float* partials, int64_t M, int
  *   partials  [splits,M,N] F32, read only; `splits` must be the value that
  *             produced them.
  *   C         [M,N] F32, written in full.
- * M must be a positive multiple of 32 and N of 64, as for the GEMM.
+ * M must be a positive multiple of 32 and N positive, as for the GEMM.
  * Returns a splitk_status.
  */
 int splitk_reduce(const float* partials, float* C, int64_t splits, int64_t M, int64_t N,
@@ -173,8 +175,9 @@ int splitk_gemm_bt_auto(const void* A, const void* B, float* workspace, int64_t 
  * method"); the operation is unchanged:
  *   partials[s,i,j] = sum_{k in slice s} A[i,k] * B[k,j].
  *   B   [K,N] elements of `dtype`, read only, resident weights.
- * Every other argument, the shape domain, the checks and the statuses are
- * those of splitk_gemm_bt (B still spans N*K elements).
+ * Every other argument, the checks and the statuses are those of
+ * splitk_gemm_bt (B still spans N*K elements), except that N must be a
+ * multiple of 8 so that every row of B starts 16-byte aligned.
  */
 int splitk_gemm_bn(const void* A, const void* B, float* partials, int64_t M, int64_t N, int64_t K,
                    int64_t k_per_split, int64_t splits, int dtype, void* stream);

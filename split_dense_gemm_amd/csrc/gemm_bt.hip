@@ -121,12 +121,30 @@ __device__ inline int kn_lds(int b) {
     return (u << 7) | (kn_slot(u, (b >> 4) & 7) << 4) | (b & 15);
 }
 
-// Global byte offset, from the first element of the split's first k-row in
-// the tile's columns, of the 16 bytes that fill slot j of unit u.
+// Global byte offset, from the split's first k-row, of the 16 bytes that
+// fill slot j of unit u for the column tile starting at byte col0.  A tail
+// tile's granules past the last column re-read the row's last granule (in
+// bounds; those columns are never stored).  Needs row_bytes_b % 16 == 0.
 template <int ES, int BN>
-__device__ inline size_t kn_src(int u, int j, size_t row_bytes_b) {
+__device__ inline size_t kn_src(int u, int j, size_t row_bytes_b, size_t col0) {
     const int byte = u * kChunkBytes + kn_slot(u, j) * 16;
-    return (size_t)(byte / (BN * ES)) * row_bytes_b + (size_t)(byte % (BN * ES));
+    size_t col = col0 + (size_t)(byte % (BN * ES));
+    if (col + 16 > row_bytes_b) col = row_bytes_b - 16;
+    return (size_t)(byte / (BN * ES)) * row_bytes_b + col;
+}
+
+// Stores columns col..col+3 of one output row of a tile.  Columns at or past
+// `valid` (those of the tile that lie inside N) are left alone, and when N
+// is not a multiple of 4 the rows are not 16-byte aligned, so the store is
+// split into 4-byte stores.
+__device__ inline void store_cols4(float* dst, f32x4 v, int col, int valid, bool vec_ok) {
+    if (vec_ok && col + 4 <= valid) {
+        *(f32x4*)dst = v;
+        return;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        if (col + e < valid) dst[e] = v[e];
 }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -214,12 +232,13 @@ __global__ __launch_bounds__(W * 64) void gemm_bt_wavek(const uint8_t* __restric
         piece[i] = slot_of(row, lslot);  // the global piece that lands in slot lslot
         if (BL == 1 && i >= BM / 8) {
             // Unit row - BM of the [CK][BN] tile; its slot lslot.
-            src[i] = B + (size_t)k0 * row_bytes_b + (size_t)nt * BN * ES +
-                     kn_src<ES, BN>(row - BM, lslot, row_bytes_b);
+            src[i] = B + (size_t)k0 * row_bytes_b +
+                     kn_src<ES, BN>(row - BM, lslot, row_bytes_b, (size_t)nt * BN * ES);
             piece[i] = 0;
         } else {
+            // B rows past N (a tail tile) re-read row N-1; never stored.
             src[i] = row < BM ? A + (size_t)(mt * BM + row) * row_bytes
-                              : B + (size_t)(nt * BN + row - BM) * row_bytes;
+                              : B + (size_t)min(nt * BN + row - BM, N - 1) * row_bytes;
             src[i] += (size_t)k0 * ES;
         }
     }
@@ -326,13 +345,26 @@ __global__ __launch_bounds__(W * 64) void gemm_bt_wavek(const uint8_t* __restric
     // Sum the W partial tiles in ascending wave order; one 16-byte store per item.
     constexpr int ROW4 = BN / 4;
     float* out = P + ((size_t)s * M + (size_t)mt * BM) * N + (size_t)nt * BN;
-    for (int it = threadIdx.x; it < BM * ROW4; it += W * 64) {
-        const int row = it / ROW4;
-        const int col = (it % ROW4) * 4;
-        f32x4 v = *(const f32x4*)&red[0][row][col];
+    const int valid = min(BN, N - nt * BN);  // columns of this tile inside N
+    const bool vec_ok = (N & 3) == 0;
+    if (valid == BN && vec_ok) {
+        for (int it = threadIdx.x; it < BM * ROW4; it += W * 64) {
+            const int row = it / ROW4;
+            const int col = (it % ROW4) * 4;
+            f32x4 v = *(const f32x4*)&red[0][row][col];
 #pragma unroll
-        for (int w = 1; w < W; ++w) v += *(const f32x4*)&red[w][row][col];
-        *(f32x4*)(out + (size_t)row * N + col) = v;
+            for (int w = 1; w < W; ++w) v += *(const f32x4*)&red[w][row][col];
+            *(f32x4*)(out + (size_t)row * N + col) = v;
+        }
+    } else {
+        for (int it = threadIdx.x; it < BM * ROW4; it += W * 64) {
+            const int row = it / ROW4;
+            const int col = (it % ROW4) * 4;
+            f32x4 v = *(const f32x4*)&red[0][row][col];
+#pragma unroll
+            for (int w = 1; w < W; ++w) v += *(const f32x4*)&red[w][row][col];
+            store_cols4(out + (size_t)row * N + col, v, col, valid, vec_ok);
+        }
     }
 }
 
@@ -421,12 +453,12 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bt_tiled(const uint8_t* __r
         const int row = 8 * (i * NW + wave) + (lane >> 3);
         piece[i] = slot_of(row, lane & 7);
         if (BL == 1 && i >= IA) {
-            src[i] = B + (size_t)k0 * row_bytes_b + (size_t)nt * BN * ES +
-                     kn_src<ES, BN>(row - BM, lane & 7, row_bytes_b);
+            src[i] = B + (size_t)k0 * row_bytes_b +
+                     kn_src<ES, BN>(row - BM, lane & 7, row_bytes_b, (size_t)nt * BN * ES);
             piece[i] = 0;
         } else {
             src[i] = (row < BM ? A + (size_t)(mt * BM + row) * row_bytes
-                               : B + (size_t)(nt * BN + row - BM) * row_bytes) +
+                               : B + (size_t)min(nt * BN + row - BM, N - 1) * row_bytes) +
                      (size_t)k0 * ES;
         }
     }
@@ -513,20 +545,38 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bt_tiled(const uint8_t* __r
     }
 
     // Register i of lane l holds row 8*(i/4) + 4*(l/32) + i%4, column l%32.
-    float* out = P + ((size_t)s * M + (size_t)mt * BM + wm * TM) * N + (size_t)nt * BN + wn * TN;
+    // The lane's own part (row 4*(l/32), column l%32) goes into one base
+    // pointer; the rest of each row offset is the same for the whole wave.
+    float* base = P + ((size_t)s * M + (size_t)mt * BM + wm * TM + 4 * h) * N + (size_t)nt * BN +
+                  wn * TN + r;
+    const int valid = N - (nt * BN + wn * TN);  // columns of this wave's sub-tile inside N
+    if (valid >= TN) {
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+        for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
+            for (int i = 0; i < 16; ++i) {
+                float* row = base + (size_t)(mb * 32 + 8 * (i >> 2) + (i & 3)) * (size_t)N;
 #pragma unroll
-            for (int i = 0; i < 16; ++i)
-                out[(size_t)(mb * 32 + 8 * (i >> 2) + 4 * h + (i & 3)) * N + nb * 32 + r] = acc[mb][nb][i];
+                for (int nb = 0; nb < NB; ++nb) row[nb * 32] = acc[mb][nb][i];
+            }
+    } else {
+        // Tail tile: only the columns inside N.
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                float* row = base + (size_t)(mb * 32 + 8 * (i >> 2) + (i & 3)) * (size_t)N;
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+                    if (nb * 32 + r < valid) row[nb * 32] = acc[mb][nb][i];
+            }
+    }
 }
 
 template <int DT, int BM, int BN, int WM, int WN, int NBUF, int BL>
 hipError_t launch_tiled(const void* A, const void* B, float* P, int64_t M, int64_t N, int64_t K,
                         int64_t kps, int64_t splits, hipStream_t stream) {
-    const int tiles_m = (int)(M / BM), tiles_n = (int)(N / BN);
+    const int tiles_m = (int)(M / BM), tiles_n = (int)((N + BN - 1) / BN);
     const dim3 grid((unsigned)(tiles_m * (int64_t)tiles_n * splits));
     const dim3 block(WM * WN * 64);
     const uint8_t* a = (const uint8_t*)A;
@@ -612,7 +662,7 @@ __global__ __launch_bounds__(W * 64) void gemm_bt_wavek_dma(const uint8_t* __res
     for (int i = 0; i < LOADS; ++i) {
         const int row = 8 * i + lrow;
         src[i] = (row < BM ? A + (size_t)(mt * BM + row) * row_bytes
-                           : B + (size_t)(nt * BN + row - BM) * row_bytes) +
+                           : B + (size_t)min(nt * BN + row - BM, N - 1) * row_bytes) +
                  (size_t)k0 * ES;
         piece[i] = slot_of(row, lane & 7);
     }
@@ -714,20 +764,33 @@ __global__ __launch_bounds__(W * 64) void gemm_bt_wavek_dma(const uint8_t* __res
     __syncthreads();
     constexpr int ROW4 = BN / 4;
     float* out = P + ((size_t)s * M + (size_t)mt * BM) * N + (size_t)nt * BN;
-    for (int it = threadIdx.x; it < BM * ROW4; it += W * 64) {
-        const int row = it / ROW4;
-        const int col = (it % ROW4) * 4;
-        f32x4 v = *(const f32x4*)&red[0][row][col];
+    const int valid = min(BN, N - nt * BN);  // columns of this tile inside N
+    const bool vec_ok = (N & 3) == 0;
+    if (valid == BN && vec_ok) {
+        for (int it = threadIdx.x; it < BM * ROW4; it += W * 64) {
+            const int row = it / ROW4;
+            const int col = (it % ROW4) * 4;
+            f32x4 v = *(const f32x4*)&red[0][row][col];
 #pragma unroll
-        for (int w = 1; w < W; ++w) v += *(const f32x4*)&red[w][row][col];
-        *(f32x4*)(out + (size_t)row * N + col) = v;
+            for (int w = 1; w < W; ++w) v += *(const f32x4*)&red[w][row][col];
+            *(f32x4*)(out + (size_t)row * N + col) = v;
+        }
+    } else {
+        for (int it = threadIdx.x; it < BM * ROW4; it += W * 64) {
+            const int row = it / ROW4;
+            const int col = (it % ROW4) * 4;
+            f32x4 v = *(const f32x4*)&red[0][row][col];
+#pragma unroll
+            for (int w = 1; w < W; ++w) v += *(const f32x4*)&red[w][row][col];
+            store_cols4(out + (size_t)row * N + col, v, col, valid, vec_ok);
+        }
     }
 }
 
 template <int DT, int BM, int BN, int W, int R>
 hipError_t launch_wavek_dma(const void* A, const void* B, float* P, int64_t M, int64_t N, int64_t K,
                             int64_t kps, int64_t splits, hipStream_t stream) {
-    const int tiles_m = (int)(M / BM), tiles_n = (int)(N / BN);
+    const int tiles_m = (int)(M / BM), tiles_n = (int)((N + BN - 1) / BN);
     const dim3 grid((unsigned)(tiles_m * (int64_t)tiles_n * splits));
     const uint8_t* a = (const uint8_t*)A;
     const uint8_t* b = (const uint8_t*)B;
@@ -740,7 +803,7 @@ hipError_t launch_wavek_dma(const void* A, const void* B, float* P, int64_t M, i
 template <int DT, int BM, int BN, int W, int D, int BL>
 hipError_t launch_wavek(const void* A, const void* B, float* P, int64_t M, int64_t N, int64_t K,
                         int64_t kps, int64_t splits, hipStream_t stream) {
-    const int tiles_m = (int)(M / BM), tiles_n = (int)(N / BN);
+    const int tiles_m = (int)(M / BM), tiles_n = (int)((N + BN - 1) / BN);
     const dim3 grid((unsigned)(tiles_m * (int64_t)tiles_n * splits));
     const dim3 block(W * 64);
     const uint8_t* a = (const uint8_t*)A;
@@ -894,18 +957,20 @@ GemmPlan plan_gemm(int dtype, int64_t M, int64_t N, int64_t K, int64_t kps, int6
     const int64_t ck = 128 / es;  // elements per 128-byte chunk
     const int64_t max_chunks = (kps + ck - 1) / ck;  // chunks of the longest split
     int fk, f[4];
-    if (forced_plan(layout, &fk, f) && M % f[0] == 0 && N % f[1] == 0 &&
+    auto cdiv = [](int64_t a, int64_t b) { return (a + b - 1) / b; };
+    if (forced_plan(layout, &fk, f) && M % f[0] == 0 &&
         (fk != kWaveKDma || max_chunks <= (int64_t)f[2] * (f[3] + 1))) {
-        const int64_t wg = (M / f[0]) * (N / f[1]) * splits;
+        const int64_t wg = (M / f[0]) * cdiv(N, f[1]) * splits;
         if (fk == kTiled) return GemmPlan{kTiled, f[0], f[1], f[2] * f[3], f[2], wg, f[2] * f[3] * 64, layout};
         return GemmPlan{fk, f[0], f[1], f[2], f[3], wg, f[2] * 64, layout};
     }
     // Large problems: 256x256 tiles (2x2 waves) when there is at least one
-    // per CU, else 256x128; these read the least L2 data per flop.
+    // per CU, else 256x128; these read the least L2 data per flop.  An N
+    // that 256 does not divide takes 256x128 tiles, the last one a tail.
     if (M % 256 == 0 && N % 256 == 0 && (M / 256) * (N / 256) * splits >= 256)
         return GemmPlan{kTiled, 256, 256, 4, 2, (M / 256) * (N / 256) * splits, 256, layout};
-    if (M % 256 == 0 && N % 128 == 0 && (M / 256) * (N / 128) * splits >= 256)
-        return GemmPlan{kTiled, 256, 128, 4, 2, (M / 256) * (N / 128) * splits, 256, layout};
+    if (M % 256 == 0 && (M / 256) * cdiv(N, 128) * splits >= 256)
+        return GemmPlan{kTiled, 256, 128, 4, 2, (M / 256) * cdiv(N, 128) * splits, 256, layout};
     // Skinny problems.  Tile: the one that moves the fewest bytes through
     // the busiest CU.  Each workgroup streams (BM + BN) rows of its split,
     // and workgroups beyond the 256 CUs queue behind the first round.
@@ -914,8 +979,8 @@ GemmPlan plan_gemm(int dtype, int64_t M, int64_t N, int64_t K, int64_t kps, int6
     int bm = 32, bn = 32;
     int64_t best_cost = -1;
     for (const Cand& c : cands) {
-        if (M % c.bm || N % c.bn) continue;
-        const int64_t wg = (M / c.bm) * (N / c.bn) * splits;
+        if (M % c.bm) continue;
+        const int64_t wg = (M / c.bm) * cdiv(N, c.bn) * splits;
         const int64_t cost = ((wg + 255) / 256) * (c.bm + c.bn) * kps * es;
         if (best_cost < 0 || cost < best_cost) { best_cost = cost; bm = c.bm; bn = c.bn; }
     }
@@ -924,7 +989,7 @@ GemmPlan plan_gemm(int dtype, int64_t M, int64_t N, int64_t K, int64_t kps, int6
     // wave's whole share of the split in flight, up to two.
     const int64_t chunks = max_chunks;
     const int w = 8;
-    const int64_t wg = (M / bm) * (N / bn) * splits;
+    const int64_t wg = (M / bm) * cdiv(N, bn) * splits;
     // Each wave's last chunk by LDS DMA whenever a wave has at most two.
     const int64_t per_wave = (chunks + w - 1) / w;
     if (layout == kLayoutNK && per_wave <= 2 && wavekdma_config_exists(bm, bn, w, (int)per_wave - 1))

@@ -3,9 +3,11 @@
 // The checks restate the launch contract of "Aligned shared rows for
 // pipelined NAX on CUDA" (section "Contract and correctness") and "Wider
 // consecutive-weight NAX GEMM" (section "Launch contract and correctness"):
-// M, K and k_per_split positive multiples of 32, N a positive multiple of 64,
-// every split starting below K with the splits covering K, exact extents and
-// outputs that alias nothing.  Each failed check returns its own status
+// M, K and k_per_split positive multiples of 32, every split starting below
+// K with the splits covering K, exact extents and outputs that alias nothing.
+// The pages also require N to be a multiple of 64; here any positive N is
+// served (a narrowed last column tile), and a multiple of 8 when B is stored
+// [K,N] so that its rows stay 16-byte aligned.  Each failed check returns its own status
 // before anything is enqueued; no HIP call is made until every check passed.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -31,11 +33,15 @@ int element_bytes(int dtype) { return dtype == SPLITK_F32 ? 4 : 2; }
 
 bool valid_dtype(int dtype) { return dtype == SPLITK_F32 || dtype == SPLITK_F16 || dtype == SPLITK_BF16; }
 
+// N granularity per layout of B: any N for [N,K], multiples of 8 for [K,N].
+int64_t n_multiple(int layout) { return layout == splitk::kLayoutKN ? 8 : 1; }
+
 // Shape, split and size checks shared by the GEMM entry points.
-int check_gemm_shape(int64_t M, int64_t N, int64_t K, int64_t kps, int64_t splits, int dtype) {
+int check_gemm_shape(int64_t M, int64_t N, int64_t K, int64_t kps, int64_t splits, int dtype,
+                     int layout = splitk::kLayoutNK) {
     if (!valid_dtype(dtype)) return SPLITK_ERR_DTYPE;
     if (M <= 0 || N <= 0 || K <= 0 || kps <= 0) return SPLITK_ERR_SHAPE;
-    if (M % 32 || K % 32 || kps % 32 || N % 64) return SPLITK_ERR_SHAPE;
+    if (M % 32 || K % 32 || kps % 32 || N % n_multiple(layout)) return SPLITK_ERR_SHAPE;
     if (M >= kMaxElems || N >= kMaxElems || K >= kMaxElems || kps >= kMaxElems) return SPLITK_ERR_RANGE;
     // Every split starts below K and together they cover K.  With kps >= 32
     // any valid split count is below K, so the products below cannot overflow.
@@ -66,7 +72,7 @@ int check_gemm_pointers(const void* A, const void* B, const float* P, const void
 int check_reduce(const float* P, const void* C, int64_t splits, int64_t M, int64_t N, int out_dtype) {
     if (!P || !C) return SPLITK_ERR_NULL;
     if (!valid_dtype(out_dtype)) return SPLITK_ERR_DTYPE;
-    if (M <= 0 || N <= 0 || M % 32 || N % 64) return SPLITK_ERR_SHAPE;
+    if (M <= 0 || N <= 0 || M % 32) return SPLITK_ERR_SHAPE;  // M*N is then a multiple of 4
     if (splits < 1) return SPLITK_ERR_SPLIT;
     if (M >= kMaxElems || N >= kMaxElems || splits >= kMaxElems) return SPLITK_ERR_RANGE;
     if (M * N >= kMaxElems || splits * (M * N) >= kMaxElems) return SPLITK_ERR_RANGE;
@@ -81,7 +87,7 @@ int check_reduce(const float* P, const void* C, int64_t splits, int64_t M, int64
 // geometry is given, so only the operands' own domain is checked).
 int check_auto_shape(int64_t M, int64_t N, int64_t K, int dtype, int out_dtype) {
     if (!valid_dtype(dtype) || !valid_dtype(out_dtype)) return SPLITK_ERR_DTYPE;
-    if (M <= 0 || N <= 0 || K <= 0 || M % 32 || K % 32 || N % 64) return SPLITK_ERR_SHAPE;
+    if (M <= 0 || N <= 0 || K <= 0 || M % 32 || K % 32) return SPLITK_ERR_SHAPE;
     if (M >= kMaxElems || N >= kMaxElems || K >= kMaxElems) return SPLITK_ERR_RANGE;
     if (M * K >= kMaxElems || N * K >= kMaxElems || M * N >= kMaxElems) return SPLITK_ERR_RANGE;
     return SPLITK_OK;
@@ -97,7 +103,7 @@ int64_t auto_workspace(int64_t splits, int64_t M, int64_t N, int out_dtype) {
 int gemm_entry(int layout, const void* A, const void* B, float* P, void* C, int64_t M, int64_t N,
                int64_t K, int64_t kps, int64_t splits, int dtype, int out_dtype, void* stream) {
     if (!A || !B || !P) return SPLITK_ERR_NULL;
-    int st = check_gemm_shape(M, N, K, kps, splits, dtype);
+    int st = check_gemm_shape(M, N, K, kps, splits, dtype, layout);
     if (st != SPLITK_OK) return st;
     if (C && !valid_dtype(out_dtype)) return SPLITK_ERR_DTYPE;
     st = check_gemm_pointers(A, B, P, C, M, N, K, splits, dtype, C ? element_bytes(out_dtype) : 0);
@@ -111,7 +117,7 @@ int gemm_entry(int layout, const void* A, const void* B, float* P, void* C, int6
 
 int describe_plan(int layout, int64_t M, int64_t N, int64_t K, int64_t k_per_split, int64_t splits,
                   int dtype, char* buf, int64_t len) {
-    int st = check_gemm_shape(M, N, K, k_per_split, splits, dtype);
+    int st = check_gemm_shape(M, N, K, k_per_split, splits, dtype, layout);
     if (st != SPLITK_OK) return st;
     const splitk::GemmPlan p = splitk::plan_gemm(dtype, M, N, K, k_per_split, splits, layout);
     if (buf && len > 0) {
@@ -136,8 +142,8 @@ const char* splitk_status_str(int status) {
         case SPLITK_ERR_NULL: return "null pointer";
         case SPLITK_ERR_DTYPE: return "unknown dtype";
         case SPLITK_ERR_SHAPE:
-            return "bad shape: M, K and k_per_split must be positive multiples of 32, N a positive "
-                   "multiple of 64";
+            return "bad shape: M, K and k_per_split must be positive multiples of 32 and N positive "
+                   "(a multiple of 8 when B is stored [K,N])";
         case SPLITK_ERR_SPLIT:
             return "bad split geometry: every split must start below K and the splits must cover K";
         case SPLITK_ERR_ALIAS: return "an output overlaps an input or the other output";

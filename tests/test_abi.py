@@ -50,8 +50,8 @@ SHAPE_CASES = [
     ((256, 1024, 2048, 1024, 2, -1), DTYPE),
     ((0, 64, 64, 32, 2, BF16), SHAPE),
     ((48, 64, 64, 32, 2, BF16), SHAPE),       # M not a multiple of 32
-    ((32, 96, 64, 32, 2, BF16), SHAPE),       # N not a multiple of 64
-    ((32, 32, 64, 32, 2, BF16), SHAPE),
+    ((32, 0, 64, 32, 2, BF16), SHAPE),        # N must be positive
+    ((32, -64, 64, 32, 2, BF16), SHAPE),
     ((32, 64, 48, 48, 1, BF16), SHAPE),       # K not a multiple of 32
     ((32, 64, 64, 16, 4, BF16), SHAPE),       # kps not a multiple of 32
     ((32, 64, -64, 32, 2, BF16), SHAPE),
@@ -157,7 +157,8 @@ class TestPointerChecksWithoutDevice:
         assert self.gemm(hip_lib, A=A_PTR + 8, M=48) == SHAPE
         assert self.gemm(hip_lib, P=A_PTR, S=3) == SPLIT
         assert hip_lib.raw_call("splitk_reduce", P_PTR, C_PTR, 0, 256, 1024, None) == SPLIT
-        assert hip_lib.raw_call("splitk_reduce", P_PTR, C_PTR, 2, 256, 96, None) == SHAPE
+        assert hip_lib.raw_call("splitk_reduce", P_PTR, C_PTR, 2, 256, 0, None) == SHAPE
+        assert hip_lib.raw_call("splitk_reduce", P_PTR, C_PTR, 2, 48, 64, None) == SHAPE
 
 
 def test_binding_rejects_host_tensors(hip_lib):
@@ -205,7 +206,7 @@ def test_choice_follows_the_measured_extremes(hip_lib):
 
 
 @pytest.mark.parametrize("args,status", [
-    ((48, 512, 1024, BF16, 0), SHAPE), ((32, 96, 1024, BF16, 0), SHAPE),
+    ((48, 512, 1024, BF16, 0), SHAPE), ((32, 0, 1024, BF16, 0), SHAPE),
     ((32, 512, 1000, BF16, 0), SHAPE), ((32, 512, 0, BF16, 0), SHAPE),
     ((32, 512, 1024, 3, 0), DTYPE), ((32, 512, 1024, BF16, 9), DTYPE),
     ((1 << 16, 64, 1 << 15, BF16, 0), RANGE),
@@ -218,6 +219,29 @@ def test_choice_checks(hip_lib, args, status):
 
 
 # ------------------------------------------------ B stored [K,N]
+
+# N tails: any positive N with B stored [N,K]; a multiple of 8 with [K,N].
+N_TAIL_CASES = [(N, OK, OK if N % 8 == 0 else SHAPE) for N in (1, 3, 8, 36, 40, 96, 100, 1000, 1030)]
+
+
+@pytest.mark.parametrize("N,status_nk,status_kn", N_TAIL_CASES)
+def test_n_tails_accepted(hip_lib, N, status_nk, status_kn):
+    buf = ctypes.create_string_buffer(128)
+    lib = hip_lib.load()
+    assert lib.splitk_describe(64, N, 1024, 256, 4, BF16, buf, len(buf)) == status_nk
+    assert lib.splitk_describe_bn(64, N, 1024, 256, 4, BF16, buf, len(buf)) == status_kn
+    if status_nk == OK:
+        kps, s, need = hip_lib.choose_splits(64, N, 1024, BF16)
+        assert (s - 1) * kps < 1024 <= s * kps
+
+
+def test_tail_tiles_in_plans(hip_lib):
+    # Column tiles are counted with the narrowed last tile included.
+    text = hip_lib.describe(2048, 4000, 1024, 256, 4, BF16)
+    assert text.startswith("tiled bm256 bn128") and text.endswith(f"grid{8 * 32 * 4}"), text
+    text = hip_lib.describe(64, 100, 1024, 256, 4, BF16)
+    assert text.endswith("grid" + str(2 * (2 if " bn64 " in text else 4) * 4)), text
+
 
 @pytest.mark.parametrize("args,status", SHAPE_CASES)
 def test_describe_bn_checks_shape_and_split(hip_lib, args, status):

@@ -44,20 +44,21 @@ KN_TILED = _configs("SPLITK_KN_TILED_CONFIGS")
 
 
 def _shape(kind, cfg):
-    """(M, N, K, kps, splits) for a configuration."""
+    """(M, N, K, kps, splits) for a configuration.  N leaves a narrowed last
+    column tile of 40 columns (a multiple of 8, as B stored [K,N] needs)."""
     bm, bn = cfg[0], cfg[1]
     if kind == "wavek":
         # 37 chunks of 32 per split: odd, so 16-bit slices end in a half
         # chunk; more chunks than waves x stages, so the pipeline loops.
-        return 3 * bm, max(2 * bn, 128), 2 * 1184 + 96, 1184, 3
+        return 3 * bm, max(2 * bn, 128) + 40, 2 * 1184 + 96, 1184, 3
     if kind == "wavekdma":
         # At most waves x (register chunks + 1) chunks per split (F32 chunks
         # hold 32 elements, 16-bit ones 64); odd multiples of 32 end 16-bit
         # slices in a half chunk, and the short last split leaves some waves
         # with fewer chunks than others.
         kps = 32 * (7 if cfg[3] == 0 else 15)
-        return 3 * bm, max(2 * bn, 128), 2 * kps + 96, kps, 3
-    return 2 * bm, 2 * bn, 2 * 608 + 32, 608, 3
+        return 3 * bm, max(2 * bn, 128) + 40, 2 * kps + 96, kps, 3
+    return 2 * bm, 2 * bn + 40, 2 * 608 + 32, 608, 3
 
 
 CASES = ([("nk", "wavek", c) for c in WAVEK] + [("nk", "wavekdma", c) for c in WAVEKDMA] +

@@ -3,7 +3,8 @@
 // partials[s,i,j] = sum over k in [s*kps, min((s+1)*kps, K)) of A[i,k]*B[j,k]
 // ("Aligned shared rows for pipelined NAX on CUDA", section "Contract and
 // correctness"; "Wider consecutive-weight NAX GEMM", section "Launch contract
-// and correctness").  A is [M,K], B is [N,K], both k-contiguous.
+// and correctness").  A is [M,K] and k-contiguous; B is [N,K] (k-contiguous)
+// or, for the [K,N] entry points, [K,N] (n-contiguous).
 //
 // The pages' own kernels (a 32x64 tile on 128 threads, 40-element padded
 // shared rows, BF16 converted to F16 on the way in) were built for other
@@ -12,26 +13,31 @@
 //  * Native MFMA on the stored element type: v_mfma_f32_32x32x16_{bf16,f16}
 //    for 16-bit inputs and v_mfma_f32_32x32x2_f32 for F32, accumulating in
 //    F32.  BF16 is never narrowed to F16.
-//  * Both operands are k-contiguous, so both MFMA fragments can be fetched
-//    straight from global memory: lane l (row l%32 of a 32-row block, half
-//    h = l/32) reads 64 consecutive bytes of its row per 128-byte chunk, as
-//    four 16-byte loads.  Piece q of that read feeds MFMA step q.  The order
-//    in which an MFMA's k slots are filled does not change the dot product,
-//    so A and B fragments only have to use the same slot -> k assignment,
-//    which they do because they are loaded identically.
-//  * In the skinny shapes of this workload the grid has only a few hundred
-//    output tiles, so the k axis of each split is shared among the waves of
-//    a workgroup (chunk c goes to wave c % W) and the W partial tiles are
-//    added through LDS in a fixed wave order before one coalesced 16-byte
-//    store per lane.  No atomics; every output element is written once.
+//  * Work unit: a 128-byte k-chunk of every row of a BM x BN tile (BM rows of
+//    A and BN rows of B).  Global loads are coalesced: each load instruction
+//    of a wave reads eight whole 128-byte row segments; the transpose into
+//    MFMA fragments happens in LDS, whose 16-byte slots are XOR-swizzled so
+//    that the fragment reads are free of bank conflicts.  The order in which
+//    an MFMA's k slots are filled does not change the dot product, so A and
+//    B fragments only have to use the same slot -> k assignment.
+//  * Three kernel families.  gemm_bt_wavek (skinny shapes): the waves of a
+//    workgroup take the split's chunks round-robin through a register
+//    pipeline and per-wave LDS staging, and their partial tiles are added
+//    through LDS in a fixed wave order.  gemm_bt_wavek_dma: the same, with
+//    each wave's last chunk loaded straight into LDS (global_load_lds).
+//    gemm_bt_tiled (large problems): a 256-row tile whose waves share every
+//    chunk, fed through a ring of LDS buffers by LDS DMA.  No atomics; every
+//    output element is written once.
 //  * Slice ends are multiples of 32 elements.  For 16-bit inputs a chunk is
-//    64 elements, so the last chunk of a slice may be half empty: those lanes
-//    skip their loads (exec-masked) and feed zeros, which adds exactly 0.
-//    No load ever touches memory past the slice, so the exact-extent rule
-//    holds for the last split of the last row.
-//  * Workgroups are renumbered so that the tiles sharing a B panel (same
-//    split and column block, different row blocks) land on one XCD and reuse
-//    it from that XCD's L2.
+//    64 elements, so the last chunk of a slice may be half empty: its loads
+//    are redirected to in-bounds data of the same slice and its upper half
+//    never reaches an MFMA (skipped steps or zeroed A fragments).  No load
+//    touches memory past the operands' ends.
+//  * Column tails: the last column tile may extend past N.  Its B rows past
+//    N re-read row N-1 (or, for [K,N], the row's last 16 bytes) and its
+//    output columns past N are never stored.
+//  * Workgroups are renumbered so that the tiles sharing operand panels run
+//    on one XCD and reuse them from that XCD's L2.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdio.h>

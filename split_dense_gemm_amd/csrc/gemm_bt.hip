@@ -139,18 +139,44 @@ __device__ inline size_t kn_src(int u, int j, size_t row_bytes_b, size_t col0) {
     return (size_t)(byte / (BN * ES)) * row_bytes_b + col;
 }
 
-// Stores columns col..col+3 of one output row of a tile.  Columns at or past
-// `valid` (those of the tile that lie inside N) are left alone, and when N
-// is not a multiple of 4 the rows are not 16-byte aligned, so the store is
-// split into 4-byte stores.
-__device__ inline void store_cols4(float* dst, f32x4 v, int col, int valid, bool vec_ok) {
-    if (vec_ok && col + 4 <= valid) {
-        *(f32x4*)dst = v;
-        return;
-    }
+// Cross-wave sum of a skinny workgroup's W partial BM x BN tiles, and its
+// store.  Each wave writes its accumulators column-major into its own LDS
+// tile: the four registers 4g..4g+3 of a 32x32 block hold four consecutive
+// rows of one column, so each group is one 16-byte write.  A column pitch of
+// BM + 4 floats steps 16 bytes further round the banks per column, which
+// keeps the lanes of a write (and of the reads below) on distinct banks.  Then
+// each thread takes one column and four rows, adds the W tiles in ascending
+// wave order and stores the four values.  Consecutive lanes hold consecutive
+// columns, so every store instruction writes whole row segments; columns at
+// or past `valid` (outside N) are not stored.  The caller has made the LDS
+// area free (a barrier after its last use).
+template <int BM, int BN, int W, int MB, int NB>
+__device__ inline void sum_and_store(float* lds, const f32x16 (&acc)[MB][NB], float* out, int N,
+                                     int valid, int wave, int lane) {
+    constexpr int CP = BM + 4;  // floats per column of one wave's tile
+    float* mine = lds + wave * BN * CP;
+    const int r = lane & 31, h = lane >> 5;
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-        if (col + e < valid) dst[e] = v[e];
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const f32x4 v = {acc[mb][nb][4 * g], acc[mb][nb][4 * g + 1], acc[mb][nb][4 * g + 2],
+                                 acc[mb][nb][4 * g + 3]};
+                *(f32x4*)(mine + (nb * 32 + r) * CP + mb * 32 + 8 * g + 4 * h) = v;
+            }
+    __syncthreads();
+    for (int it = threadIdx.x; it < BN * (BM / 4); it += W * 64) {
+        const int col = it % BN, rq = it / BN;
+        f32x4 v = *(const f32x4*)(lds + col * CP + 4 * rq);
+#pragma unroll
+        for (int w = 1; w < W; ++w) v += *(const f32x4*)(lds + (w * BN + col) * CP + 4 * rq);
+        if (col < valid) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) out[(size_t)(4 * rq + e) * N + col] = v[e];
+        }
+    }
 }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -198,14 +224,12 @@ __global__ __launch_bounds__(W * 64) void gemm_bt_wavek(const uint8_t* __restric
     constexpr int MB = BM / 32, NB = BN / 32;
     constexpr int ROWS = BM + BN;         // staged rows per chunk: A rows, then B rows
     constexpr int LOADS = ROWS / 8;       // 16-byte loads per lane per chunk
-    constexpr int PITCH = BN + 8;         // floats per row of the LDS reduction tile
     static_assert(ROWS % 8 == 0, "tile rows");
     // One LDS block: per-wave staging buffers during the k loop, then (after
     // a barrier) the W partial tiles of the cross-wave sum.
     constexpr int STAGE_BYTES = W * ROWS * kChunkBytes;
-    constexpr int RED_BYTES = W * BM * PITCH * 4;
+    constexpr int RED_BYTES = W * BN * (BM + 4) * 4;  // sum_and_store's tiles
     __shared__ __attribute__((aligned(16))) uint8_t smem[STAGE_BYTES > RED_BYTES ? STAGE_BYTES : RED_BYTES];
-    float (*red)[BM][PITCH] = reinterpret_cast<float (*)[BM][PITCH]>(smem);
 
     const int logical = xcd_logical_id(blockIdx.x, gridDim.x);
     const int mt = logical % tiles_m;
@@ -337,41 +361,9 @@ __global__ __launch_bounds__(W * 64) void gemm_bt_wavek(const uint8_t* __restric
         if (t + j < mine) compute(chunk_of(t + j), stg[j]);
 
     __syncthreads();  // every wave is done with its staging buffer
-    // 32x32 accumulator layout: register i of lane l holds
-    // row 8*(i/4) + 4*(l/32) + i%4, column l%32 of the block.
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                red[wave][mb * 32 + 8 * (i >> 2) + 4 * h + (i & 3)][nb * 32 + r] = acc[mb][nb][i];
-    __syncthreads();
-
-    // Sum the W partial tiles in ascending wave order; one 16-byte store per item.
-    constexpr int ROW4 = BN / 4;
-    float* out = P + ((size_t)s * M + (size_t)mt * BM) * N + (size_t)nt * BN;
-    const int valid = min(BN, N - nt * BN);  // columns of this tile inside N
-    const bool vec_ok = (N & 3) == 0;
-    if (valid == BN && vec_ok) {
-        for (int it = threadIdx.x; it < BM * ROW4; it += W * 64) {
-            const int row = it / ROW4;
-            const int col = (it % ROW4) * 4;
-            f32x4 v = *(const f32x4*)&red[0][row][col];
-#pragma unroll
-            for (int w = 1; w < W; ++w) v += *(const f32x4*)&red[w][row][col];
-            *(f32x4*)(out + (size_t)row * N + col) = v;
-        }
-    } else {
-        for (int it = threadIdx.x; it < BM * ROW4; it += W * 64) {
-            const int row = it / ROW4;
-            const int col = (it % ROW4) * 4;
-            f32x4 v = *(const f32x4*)&red[0][row][col];
-#pragma unroll
-            for (int w = 1; w < W; ++w) v += *(const f32x4*)&red[w][row][col];
-            store_cols4(out + (size_t)row * N + col, v, col, valid, vec_ok);
-        }
-    }
+    sum_and_store<BM, BN, W, MB, NB>(reinterpret_cast<float*>(smem), acc,
+                                     P + ((size_t)s * M + (size_t)mt * BM) * N + (size_t)nt * BN, N,
+                                     min(BN, N - nt * BN), wave, lane);
 }
 
 // s_waitcnt immediate that waits until at most n vector-memory operations
@@ -629,16 +621,14 @@ __global__ __launch_bounds__(W * 64) void gemm_bt_wavek_dma(const uint8_t* __res
     constexpr int ROWS = BM + BN;
     constexpr int LOADS = ROWS / 8;
     constexpr int BLOCK = 32 * kChunkBytes;          // one 32-row block of a chunk
-    constexpr int PITCH = BN + 4;
     static_assert(LOADS < 64 && R * LOADS + LOADS < 64, "vmcnt range");
-    static_assert(W * BM * PITCH * 4 <= W * ROWS * kChunkBytes, "reduction tile fits the DMA area");
+    static_assert(W * BN * (BM + 4) * 4 <= W * ROWS * kChunkBytes, "reduction tiles fit the DMA area");
     // Separate LDS objects for the transpose blocks and the DMA chunks, so
     // the compiler can see that writing a transpose block does not have to
     // wait for the DMA still in flight.  The reduction tile reuses the DMA
     // area after a barrier.
     __shared__ __attribute__((aligned(16))) uint8_t tr_lds[W][BLOCK];
     __shared__ __attribute__((aligned(16))) uint8_t dma_lds[W][ROWS * kChunkBytes];
-    float (*red)[BM][PITCH] = reinterpret_cast<float (*)[BM][PITCH]>(&dma_lds[0][0]);
 
     const int logical = xcd_logical_id(blockIdx.x, gridDim.x);
     const int mt = logical % tiles_m;
@@ -758,39 +748,9 @@ __global__ __launch_bounds__(W * 64) void gemm_bt_wavek_dma(const uint8_t* __res
     }
 
     __syncthreads();  // every wave is done with its LDS areas
-    // Operands were not swapped: register i of lane l holds row
-    // 8*(i/4) + 4*(l/32) + i%4, column l%32 of the block.
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                red[wave][mb * 32 + 8 * (i >> 2) + 4 * h + (i & 3)][nb * 32 + r] = acc[mb][nb][i];
-    __syncthreads();
-    constexpr int ROW4 = BN / 4;
-    float* out = P + ((size_t)s * M + (size_t)mt * BM) * N + (size_t)nt * BN;
-    const int valid = min(BN, N - nt * BN);  // columns of this tile inside N
-    const bool vec_ok = (N & 3) == 0;
-    if (valid == BN && vec_ok) {
-        for (int it = threadIdx.x; it < BM * ROW4; it += W * 64) {
-            const int row = it / ROW4;
-            const int col = (it % ROW4) * 4;
-            f32x4 v = *(const f32x4*)&red[0][row][col];
-#pragma unroll
-            for (int w = 1; w < W; ++w) v += *(const f32x4*)&red[w][row][col];
-            *(f32x4*)(out + (size_t)row * N + col) = v;
-        }
-    } else {
-        for (int it = threadIdx.x; it < BM * ROW4; it += W * 64) {
-            const int row = it / ROW4;
-            const int col = (it % ROW4) * 4;
-            f32x4 v = *(const f32x4*)&red[0][row][col];
-#pragma unroll
-            for (int w = 1; w < W; ++w) v += *(const f32x4*)&red[w][row][col];
-            store_cols4(out + (size_t)row * N + col, v, col, valid, vec_ok);
-        }
-    }
+    sum_and_store<BM, BN, W, MB, NB>(reinterpret_cast<float*>(&dma_lds[0][0]), acc,
+                                     P + ((size_t)s * M + (size_t)mt * BM) * N + (size_t)nt * BN, N,
+                                     min(BN, N - nt * BN), wave, lane);
 }
 
 template <int DT, int BM, int BN, int W, int R>

@@ -115,28 +115,41 @@ __device__ inline int slot_of(int r, int p) { return p ^ (r & 7) ^ ((r >> 3) & 1
 //
 // A chunk of B is then CK k-rows of the tile's BN columns: CK*BN*ES bytes,
 // the same 128 bytes per column as in the [N,K] case, held in LDS as the
-// dense [CK][BN] tile cut into 128-byte units (unit u = bytes 128u..128u+127
-// of the tile).  Granule p (16 bytes) of unit u sits in slot p ^ (u & 2);
-// the flip of granule bit 1 on every other pair of units keeps the
-// transposing fragment reads below off each other's banks.
-__device__ inline int kn_slot(int u, int p) { return p ^ (u & 2); }
+// dense [CK][BN] tile.  Within each k-row the 16-byte granules are permuted
+// (granule g sits at g ^ kn_flip(k-row)) so that the transposing fragment
+// reads below, which take 4 consecutive k-rows x 64 bytes at once, meet 16
+// distinct granule positions modulo the 256 bytes of the LDS banks.
+// Granule positions modulo 16 of k-row r start at r * (granules per row):
+// rows of 64 bytes already land in distinct quarters, rows of 128 bytes
+// alternate halves and need the 64-byte block flipped on every other pair,
+// and rows of 256 bytes or more all start at 0 and take the block index
+// XOR r % 4.  The permutation stays inside a row, so each DMA instruction
+// still fetches whole row segments.
+template <int ES, int BN>
+__device__ inline int kn_flip(int krow) {
+    constexpr int RG = BN * ES / 16;  // granules per k-row
+    return RG >= 16 ? 4 * (krow & 3) : (RG == 8 ? 4 * ((krow >> 1) & 1) : 0);
+}
 
-// LDS byte offset, inside the B tile, of byte b of the dense [CK][BN] tile.
-__device__ inline int kn_lds(int b) {
-    const int u = b >> 7;
-    return (u << 7) | (kn_slot(u, (b >> 4) & 7) << 4) | (b & 15);
+// LDS byte offset, inside the B tile, of byte colb of k-row krow.
+template <int ES, int BN>
+__device__ inline int kn_lds(int krow, int colb) {
+    return krow * BN * ES + (((colb >> 4) ^ kn_flip<ES, BN>(krow)) << 4) + (colb & 15);
 }
 
 // Global byte offset, from the split's first k-row, of the 16 bytes that
-// fill slot j of unit u for the column tile starting at byte col0.  A tail
+// fill slot j of 128-byte unit u of the tile (the tile is filled unit by
+// unit in LDS order) for the column tile starting at byte col0.  A tail
 // tile's granules past the last column re-read the row's last granule (in
 // bounds; those columns are never stored).  Needs row_bytes_b % 16 == 0.
 template <int ES, int BN>
 __device__ inline size_t kn_src(int u, int j, size_t row_bytes_b, size_t col0) {
-    const int byte = u * kChunkBytes + kn_slot(u, j) * 16;
-    size_t col = col0 + (size_t)(byte % (BN * ES));
+    constexpr int RG = BN * ES / 16;
+    const int pg = u * 8 + j;  // granule position in the tile
+    const int krow = pg / RG;
+    size_t col = col0 + (size_t)(((pg % RG) ^ kn_flip<ES, BN>(krow)) * 16);
     if (col + 16 > row_bytes_b) col = row_bytes_b - 16;
-    return (size_t)(byte / (BN * ES)) * row_bytes_b + col;
+    return (size_t)krow * row_bytes_b + col;
 }
 
 // Cross-wave sum of a skinny workgroup's W partial BM x BN tiles, and its
@@ -197,7 +210,7 @@ __device__ inline u32x4 kn_frag(const uint8_t* tile, int q, int nb, int lane) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int krow = 8 * q + 4 * (lane >> 5) + e;
-            v[e] = *(const uint32_t*)(tile + kn_lds(krow * BN * 4 + (nb * 32 + (lane & 31)) * 4));
+            v[e] = *(const uint32_t*)(tile + kn_lds<4, BN>(krow, (nb * 32 + (lane & 31)) * 4));
         }
         return v;
     } else {
@@ -205,8 +218,8 @@ __device__ inline u32x4 kn_frag(const uint8_t* tile, int q, int nb, int lane) {
         const int krow = 16 * q + 8 * (g >> 1) + ((lane >> 2) & 3);
         const int colb = (nb * 32 + 16 * (g & 1) + 4 * (lane & 3)) * 2;
         typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + kn_lds(krow * BN * 2 + colb)));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + kn_lds((krow + 4) * BN * 2 + colb)));
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + kn_lds<2, BN>(krow, colb)));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + kn_lds<2, BN>(krow + 4, colb)));
         typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
         const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
         return u32x4{l2.x, l2.y, h2.x, h2.y};

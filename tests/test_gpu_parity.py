@@ -122,6 +122,7 @@ EXTRA_SHAPES = [
     (64, 128, 2048, 32, 64),    # 64 splits of 32
     (160, 192, 608, 96, 7),     # five row blocks, seven splits, final split 32
     (32, 64, 64, 64, 1),        # one split
+    (256, 512, 2048, 512, 4),   # the pages' 256x512x2048 row at four splits
 ]
 
 
@@ -172,6 +173,15 @@ def test_closed_forms_on_gpu(sdg):
     want = b[:, :M].to(torch.float32).T.numpy()
     np.testing.assert_array_equal(run.C, want)
     np.testing.assert_array_equal(run.P[0], want)
+    assert np.all(run.P[1] == 0)
+    # One-hot B (B[j,k] = [k == j], K >= N): C[i,j] = A[i,j], pinning the
+    # row-major orientation of A and of the output.
+    M, N, K = 96, 128, 256
+    a, _ = inputs.make_operands(M, N, K, "f16", seed=8)
+    b = torch.eye(N, K, dtype=torch.float16)
+    run = Run(sdg, a, b, 128, 2, poison="nan")
+    np.testing.assert_array_equal(run.C, a[:, :N].to(torch.float32).numpy())
+    np.testing.assert_array_equal(run.P[0], a[:, :N].to(torch.float32).numpy())
     assert np.all(run.P[1] == 0)
 
 

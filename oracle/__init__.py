@@ -7,6 +7,7 @@ from .ref import (  # noqa: F401
     build,
     decode,
     encode,
+    ensure_built,
     gemm_bt,
     normalized_error,
     sampled,

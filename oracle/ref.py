@@ -42,6 +42,14 @@ def build() -> str:
     return _SO
 
 
+def ensure_built():
+    """Builds (if missing or older than oracle.c) and loads the reference.
+    Call it before the process touches the GPU: building starts the host
+    compiler, and a process that has initialised the GPU must not start
+    other programs."""
+    _load()
+
+
 def _load():
     global _lib
     if _lib is not None:

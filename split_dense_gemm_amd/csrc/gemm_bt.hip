@@ -226,6 +226,12 @@ __device__ inline u32x4 kn_frag(const uint8_t* tile, int q, int nb, int lane) {
     }
 }
 
+// Skinny kernel: one BM x BN output tile of one split per workgroup.  Its W
+// waves take the split's chunks round-robin (chunk c goes to wave c % W);
+// each wave loads its chunks with coalesced 16-byte loads into registers, D
+// chunks ahead, stages each in its own LDS area and reads MFMA fragments
+// back, so waves never wait for one another until the cross-wave sum.  BL
+// selects the layout of B ([N,K] or [K,N]).
 template <int DT, int BM, int BN, int W, int D, int BL>
 __global__ __launch_bounds__(W * 64) void gemm_bt_wavek(const uint8_t* __restrict__ A,
                                                         const uint8_t* __restrict__ B,

@@ -8,17 +8,17 @@ namespace splitk {
 
 // Which GEMM kernel family serves a call.
 enum GemmKind : int {
-    // Every wave of a workgroup computes the whole BM x BN tile over its own
-    // share of the split's 128-byte k-chunks, loading MFMA fragments straight
-    // from global memory; the waves' accumulators are summed through LDS.
-    // Suited to the skinny, short shapes (M <= 256) where the grid is small.
+    // Skinny shapes (few output tiles): the W waves of a workgroup take the
+    // split's 128-byte k-chunks round-robin, each staging its chunks through
+    // registers and a private LDS area (`stages` chunks in flight), and their
+    // partial tiles are summed through LDS in a fixed wave order.
     kWaveK = 0,
-    // A BM x BN tile per workgroup; its waves split the tile (WM x WN) and
-    // share each staged chunk through double-buffered LDS.  For large
-    // problems with enough tiles to fill the chip.
+    // Large problems with enough tiles to fill the chip: a BM x BN tile per
+    // workgroup whose WM x WN waves share every chunk, fed by LDS DMA through
+    // a ring of LDS buffers (`stages` = waves along M).
     kTiled = 1,
     // As kWaveK, but each wave's last chunk travels by LDS DMA; for splits
-    // short enough that a wave holds at most STAGES + 1 chunks.
+    // short enough that a wave holds at most `stages` + 1 chunks.
     kWaveKDma = 2,
 };
 

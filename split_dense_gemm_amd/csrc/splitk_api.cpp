@@ -7,8 +7,9 @@
 // K with the splits covering K, exact extents and outputs that alias nothing.
 // The pages also require N to be a multiple of 64; here any positive N is
 // served (a narrowed last column tile), and a multiple of 8 when B is stored
-// [K,N] so that its rows stay 16-byte aligned.  Each failed check returns its own status
-// before anything is enqueued; no HIP call is made until every check passed.
+// [K,N] so that its rows stay 16-byte aligned.  Each failed check returns its
+// own status before anything is enqueued; no HIP call is made until every
+// check has passed.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -158,15 +159,8 @@ const char* splitk_status_str(int status) {
 
 int splitk_gemm_bt(const void* A, const void* B, float* partials, int64_t M, int64_t N, int64_t K,
                    int64_t k_per_split, int64_t splits, int dtype, void* stream) {
-    if (!A || !B || !partials) return SPLITK_ERR_NULL;
-    int st = check_gemm_shape(M, N, K, k_per_split, splits, dtype);
-    if (st != SPLITK_OK) return st;
-    st = check_gemm_pointers(A, B, partials, nullptr, M, N, K, splits, dtype, 0);
-    if (st != SPLITK_OK) return st;
-    const splitk::GemmPlan plan = splitk::plan_gemm(dtype, M, N, K, k_per_split, splits);
-    hipError_t e = splitk::launch_gemm_bt(plan, A, B, partials, M, N, K, k_per_split, splits, dtype,
-                                          (hipStream_t)stream);
-    return e == hipSuccess ? SPLITK_OK : SPLITK_ERR_LAUNCH;
+    return gemm_entry(splitk::kLayoutNK, A, B, partials, nullptr, M, N, K, k_per_split, splits, dtype,
+                      SPLITK_F32, stream);
 }
 
 int splitk_reduce_typed(const float* partials, void* C, int64_t splits, int64_t M, int64_t N,
@@ -184,18 +178,9 @@ int splitk_reduce(const float* partials, float* C, int64_t splits, int64_t M, in
 int splitk_gemm_bt_reduce_typed(const void* A, const void* B, float* partials, void* C, int64_t M,
                                 int64_t N, int64_t K, int64_t k_per_split, int64_t splits, int dtype,
                                 int out_dtype, void* stream) {
-    if (!A || !B || !partials || !C) return SPLITK_ERR_NULL;
-    int st = check_gemm_shape(M, N, K, k_per_split, splits, dtype);
-    if (st != SPLITK_OK) return st;
-    if (!valid_dtype(out_dtype)) return SPLITK_ERR_DTYPE;
-    st = check_gemm_pointers(A, B, partials, C, M, N, K, splits, dtype, element_bytes(out_dtype));
-    if (st != SPLITK_OK) return st;
-    const splitk::GemmPlan plan = splitk::plan_gemm(dtype, M, N, K, k_per_split, splits);
-    hipError_t e = splitk::launch_gemm_bt(plan, A, B, partials, M, N, K, k_per_split, splits, dtype,
-                                          (hipStream_t)stream);
-    if (e != hipSuccess) return SPLITK_ERR_LAUNCH;
-    e = splitk::launch_slab_reduce(partials, C, splits, M, N, out_dtype, (hipStream_t)stream);
-    return e == hipSuccess ? SPLITK_OK : SPLITK_ERR_LAUNCH;
+    if (!C) return SPLITK_ERR_NULL;
+    return gemm_entry(splitk::kLayoutNK, A, B, partials, C, M, N, K, k_per_split, splits, dtype,
+                      out_dtype, stream);
 }
 
 int splitk_gemm_bt_reduce(const void* A, const void* B, float* partials, float* C, int64_t M,

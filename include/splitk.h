@@ -123,6 +123,24 @@ int splitk_reduce_typed(const float* partials, void* C, int64_t splits, int64_t 
                         int out_dtype, void* stream);
 
 /*
+ * The accumulation pass of splitk_reduce_typed for slabs that splitk_gemm_bt
+ * or splitk_gemm_bn has written with this geometry (M, N, K, k_per_split,
+ * splits, dtype).  The result is the same sum, bit for bit (first page,
+ * "Contract and correctness": the separate elementwise accumulation); only
+ * the order in which workgroups visit the plane differs.  After the
+ * small-tile GEMM kernels, each workgroup takes one output tile and runs on
+ * the XCD that wrote that tile's slabs, so it reads them from that XCD's L2
+ * instead of from memory.  The fused calls run this pass.
+ *   partials, C, out_dtype   as for splitk_reduce_typed.
+ *   K, k_per_split, dtype    the GEMM's, checked as for splitk_gemm_bt.
+ * Returns the statuses of splitk_reduce_typed and of splitk_gemm_bt's shape
+ * and split checks; nothing is enqueued on an error.
+ */
+int splitk_reduce_for_gemm(const float* partials, void* C, int64_t M, int64_t N, int64_t K,
+                           int64_t k_per_split, int64_t splits, int dtype, int out_dtype,
+                           void* stream);
+
+/*
  * splitk_gemm_bt then splitk_reduce_typed on the same stream.  C is [M,N] of
  * out_dtype; all arguments are checked before either kernel is enqueued.
  */

@@ -21,4 +21,5 @@ from ._lib import (  # noqa: F401
     load,
     raw_call,
     reduce,
+    reduce_for_gemm,
 )

@@ -77,6 +77,8 @@ def load():
     lib.splitk_describe_bn.restype = I
     lib.splitk_status_str.argtypes = [I]
     lib.splitk_status_str.restype = ctypes.c_char_p
+    lib.splitk_reduce_for_gemm.argtypes = [P, P, I64, I64, I64, I64, I64, I, I, P]
+    lib.splitk_reduce_for_gemm.restype = I
     lib.splitk_describe.argtypes = [I64, I64, I64, I64, I64, I, ctypes.c_char_p, I64]
     lib.splitk_describe.restype = I
     _lib = lib
@@ -177,6 +179,22 @@ def reduce(partials: torch.Tensor, C: torch.Tensor, splits: int, stream=None) ->
     else:
         _check(load().splitk_reduce_typed(partials.data_ptr(), C.data_ptr(), int(splits), M, N, out,
                                           _stream(stream)))
+    return C
+
+
+def reduce_for_gemm(partials: torch.Tensor, C: torch.Tensor, K: int, k_per_split: int, splits: int,
+                    dtype, stream=None) -> torch.Tensor:
+    """The slab sum of reduce(), for slabs a GEMM of this geometry (K,
+    k_per_split, splits, input dtype) has written: the same result bit for
+    bit, visiting the plane in that GEMM's tile order (see splitk.h)."""
+    if C.dim() != 2:
+        raise ValueError("C must be [M,N]")
+    M, N = C.shape
+    out = _out(C, M * N)
+    _f32_out(partials, "partials", splits * M * N)
+    _check(load().splitk_reduce_for_gemm(partials.data_ptr(), C.data_ptr(), M, N, int(K),
+                                         int(k_per_split), int(splits), _code(dtype), out,
+                                         _stream(stream)))
     return C
 
 

@@ -94,13 +94,19 @@ struct Mfma<0> {  // F32: four 32x32x2 MFMAs per 4-element piece, one element ea
     }
 };
 
-// Renumbers workgroups so that consecutive logical ids run on one XCD.
-// Workgroup b is dispatched to XCD b % 8; logical ids [start_x, start_x+cnt_x)
-// go to XCD x.  It is a bijection on [0, n) whatever the dispatch order.
-__device__ inline int xcd_logical_id(int b, int n) {
-    const int q = n >> 3, r = n & 7;
-    const int x = b & 7, slot = b >> 3;
-    return x < r ? x * (q + 1) + slot : r * (q + 1) + (x - r) * q + slot;
+// Output tile and split of skinny workgroup b (of n = tiles_m * tiles_n *
+// splits).  Logical ids run split fastest, then row tile, then column tile,
+// and each XCD takes a contiguous range of them: all the slabs of a tile are
+// written on one XCD, and an XCD's tiles share column panels of B.  The slab
+// sum that follows (slab_reduce_tiles) visits the tiles in the same order, so
+// that it reads the slabs from the L2 of the XCD that wrote them.
+__device__ inline void skinny_tile(int b, int n, int tiles_m, int tiles_n, int* mt, int* nt, int* s) {
+    const int splits = n / (tiles_m * tiles_n);
+    const int logical = xcd_logical_id(b, n);
+    *s = logical % splits;
+    const int u = logical / splits;
+    *mt = u % tiles_m;
+    *nt = u / tiles_m;
 }
 
 // LDS slot of 16-byte piece p of staged row r.  XOR-swizzled so that the
@@ -250,11 +256,8 @@ __global__ __launch_bounds__(W * 64) void gemm_bt_wavek(const uint8_t* __restric
     constexpr int RED_BYTES = W * BN * (BM + 4) * 4;  // sum_and_store's tiles
     __shared__ __attribute__((aligned(16))) uint8_t smem[STAGE_BYTES > RED_BYTES ? STAGE_BYTES : RED_BYTES];
 
-    const int logical = xcd_logical_id(blockIdx.x, gridDim.x);
-    const int mt = logical % tiles_m;
-    const int rest = logical / tiles_m;
-    const int nt = rest % tiles_n;
-    const int s = rest / tiles_n;
+    int mt, nt, s;
+    skinny_tile(blockIdx.x, gridDim.x, tiles_m, tiles_n, &mt, &nt, &s);
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -604,17 +607,17 @@ hipError_t launch_tiled(const void* A, const void* B, float* P, int64_t M, int64
                            0, stream);
 }
 
-// Instantiated large-tile configurations: (BM, BN, WM, WN); the LDS ring
-// holds as many chunk buffers as fit in 160 KiB, up to four.
+// Instantiated shared-ring configurations: (BM, BN, WM, WN, NBUF), NBUF
+// chunk buffers in the LDS ring (at most 160 KiB).
 #define SPLITK_TILED_CONFIGS(X) \
-    X(256, 256, 2, 2)           \
-    X(256, 128, 2, 2)           \
-    X(256, 128, 2, 4)           \
-    X(128, 128, 2, 2)
+    X(256, 256, 2, 2, 2)        \
+    X(256, 128, 2, 2, 3)        \
+    X(256, 128, 2, 4, 3)        \
+    X(128, 128, 2, 2, 4)
 
-template <int BM, int BN>
-constexpr int tiled_nbuf() {
-    return (160 * 1024) / ((BM + BN) * kChunkBytes) > 4 ? 4 : (160 * 1024) / ((BM + BN) * kChunkBytes);
+// Default ring depth of a tile: as many buffers as fit in 160 KiB, up to four.
+constexpr int tiled_nbuf(int bm, int bn) {
+    return (160 * 1024) / ((bm + bn) * kChunkBytes) > 4 ? 4 : (160 * 1024) / ((bm + bn) * kChunkBytes);
 }
 
 // Skinny kernel with the last chunk by LDS DMA.  Same work split as
@@ -649,11 +652,8 @@ __global__ __launch_bounds__(W * 64) void gemm_bt_wavek_dma(const uint8_t* __res
     __shared__ __attribute__((aligned(16))) uint8_t tr_lds[W][BLOCK];
     __shared__ __attribute__((aligned(16))) uint8_t dma_lds[W][ROWS * kChunkBytes];
 
-    const int logical = xcd_logical_id(blockIdx.x, gridDim.x);
-    const int mt = logical % tiles_m;
-    const int rest = logical / tiles_m;
-    const int nt = rest % tiles_n;
-    const int s = rest / tiles_n;
+    int mt, nt, s;
+    skinny_tile(blockIdx.x, gridDim.x, tiles_m, tiles_n, &mt, &nt, &s);
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -832,9 +832,9 @@ hipError_t launch_wavek(const void* A, const void* B, float* P, int64_t M, int64
     X(32, 64, 8, 2)
 
 #define SPLITK_KN_TILED_CONFIGS(X) \
-    X(256, 256, 2, 2)              \
-    X(256, 128, 2, 2)              \
-    X(256, 128, 2, 4)
+    X(256, 256, 2, 2, 2)           \
+    X(256, 128, 2, 2, 3)           \
+    X(256, 128, 2, 4, 3)
 
 template <int DT>
 hipError_t launch_dtype_kn(const GemmPlan& p, const void* A, const void* B, float* P, int64_t M,
@@ -847,9 +847,10 @@ hipError_t launch_dtype_kn(const GemmPlan& p, const void* A, const void* B, floa
 #undef X
     }
     if (p.kind == kTiled) {
-#define X(cbm, cbn, cwm, cwn)                                                     \
-    if (p.bm == cbm && p.bn == cbn && p.waves == cwm * cwn && p.stages == cwm)    \
-        return launch_tiled<DT, cbm, cbn, cwm, cwn, tiled_nbuf<cbm, cbn>(), 1>(A, B, P, M, N, K, kps, splits, st);
+#define X(cbm, cbn, cwm, cwn, cnb)                                                \
+    if (p.bm == cbm && p.bn == cbn && p.waves == cwm * cwn && p.stages == cwm &&  \
+        p.nbuf == cnb)                                                            \
+        return launch_tiled<DT, cbm, cbn, cwm, cwn, cnb, 1>(A, B, P, M, N, K, kps, splits, st);
         SPLITK_KN_TILED_CONFIGS(X)
 #undef X
     }
@@ -875,9 +876,10 @@ hipError_t launch_dtype(const GemmPlan& p, const void* A, const void* B, float* 
 #undef X
     }
     if (p.kind == kTiled) {
-#define X(cbm, cbn, cwm, cwn)                                                     \
-    if (p.bm == cbm && p.bn == cbn && p.waves == cwm * cwn && p.stages == cwm)    \
-        return launch_tiled<DT, cbm, cbn, cwm, cwn, tiled_nbuf<cbm, cbn>(), 0>(A, B, P, M, N, K, kps, splits, st);
+#define X(cbm, cbn, cwm, cwn, cnb)                                                \
+    if (p.bm == cbm && p.bn == cbn && p.waves == cwm * cwn && p.stages == cwm &&  \
+        p.nbuf == cnb)                                                            \
+        return launch_tiled<DT, cbm, cbn, cwm, cwn, cnb, 0>(A, B, P, M, N, K, kps, splits, st);
         SPLITK_TILED_CONFIGS(X)
 #undef X
     }
@@ -906,9 +908,9 @@ bool wavek_config_exists(int layout, int bm, int bn, int w, int d) {
 
 }  // namespace
 
-bool tiled_config_exists(int layout, int bm, int bn, int wm, int wn) {
-#define X(cbm, cbn, cwm, cwn) \
-    if (bm == cbm && bn == cbn && wm == cwm && wn == cwn) return true;
+bool tiled_config_exists(int layout, int bm, int bn, int wm, int wn, int nbuf) {
+#define X(cbm, cbn, cwm, cwn, cnb) \
+    if (bm == cbm && bn == cbn && wm == cwm && wn == cwn && nbuf == cnb) return true;
     if (layout == kLayoutKN) {
         SPLITK_KN_TILED_CONFIGS(X)
         return false;
@@ -926,28 +928,39 @@ bool tiled_config_exists(int layout, int bm, int bn, int wm, int wn) {
 static bool forced_plan(int layout, int* kind, int* v) {
     const char* e = getenv("SPLITK_PLAN");
     char name[16] = {0};  // "wavek", "wavekdma" or "tiled"
-    if (!e || sscanf(e, "%15[a-z],%d,%d,%d,%d", name, &v[0], &v[1], &v[2], &v[3]) != 5) return false;
-    if (!strcmp(name, "wavek") && wavek_config_exists(layout, v[0], v[1], v[2], v[3])) { *kind = kWaveK; return true; }
-    if (!strcmp(name, "wavekdma") && layout == kLayoutNK && wavekdma_config_exists(v[0], v[1], v[2], v[3])) {
+    v[4] = 0;
+    const int got = e ? sscanf(e, "%15[a-z],%d,%d,%d,%d,%d", name, &v[0], &v[1], &v[2], &v[3], &v[4]) : 0;
+    if (got != 5 && got != 6) return false;
+    if (!strcmp(name, "wavek") && got == 5 && wavek_config_exists(layout, v[0], v[1], v[2], v[3])) {
+        *kind = kWaveK;
+        return true;
+    }
+    if (!strcmp(name, "wavekdma") && got == 5 && layout == kLayoutNK &&
+        wavekdma_config_exists(v[0], v[1], v[2], v[3])) {
         *kind = kWaveKDma;
         return true;
     }
-    if (!strcmp(name, "tiled") && tiled_config_exists(layout, v[0], v[1], v[2], v[3])) { *kind = kTiled; return true; }
+    if (!strcmp(name, "tiled")) {
+        if (got == 5) v[4] = tiled_nbuf(v[0], v[1]);
+        if (tiled_config_exists(layout, v[0], v[1], v[2], v[3], v[4])) { *kind = kTiled; return true; }
+    }
     return false;
 }
 
-GemmPlan plan_gemm(int dtype, int64_t M, int64_t N, int64_t K, int64_t kps, int64_t splits,
-                   int layout) {
+// The configuration the shape rules pick (or the override forces).
+static GemmPlan plan_by_shape(int dtype, int64_t M, int64_t N, int64_t K, int64_t kps,
+                              int64_t splits, int layout) {
     (void)K;
     const int64_t es = dtype == 0 ? 4 : 2;
     const int64_t ck = 128 / es;  // elements per 128-byte chunk
     const int64_t max_chunks = (kps + ck - 1) / ck;  // chunks of the longest split
-    int fk, f[4];
+    int fk, f[5];
     auto cdiv = [](int64_t a, int64_t b) { return (a + b - 1) / b; };
     if (forced_plan(layout, &fk, f) && M % f[0] == 0 &&
         (fk != kWaveKDma || max_chunks <= (int64_t)f[2] * (f[3] + 1))) {
         const int64_t wg = (M / f[0]) * cdiv(N, f[1]) * splits;
-        if (fk == kTiled) return GemmPlan{kTiled, f[0], f[1], f[2] * f[3], f[2], wg, f[2] * f[3] * 64, layout};
+        if (fk == kTiled)
+            return GemmPlan{kTiled, f[0], f[1], f[2] * f[3], f[2], wg, f[2] * f[3] * 64, layout, f[4]};
         return GemmPlan{fk, f[0], f[1], f[2], f[3], wg, f[2] * 64, layout};
     }
     // Large problems: 256x256 tiles (2x2 waves) when there is at least one
@@ -956,9 +969,11 @@ GemmPlan plan_gemm(int dtype, int64_t M, int64_t N, int64_t K, int64_t kps, int6
     // flop.  An N that 256 does not divide takes 256x128 tiles, the last one
     // a tail.
     if (M % 256 == 0 && N % 256 == 0 && (M / 256) * (N / 256) * splits >= 256)
-        return GemmPlan{kTiled, 256, 256, 4, 2, (M / 256) * (N / 256) * splits, 256, layout};
+        return GemmPlan{kTiled, 256, 256, 4, 2, (M / 256) * (N / 256) * splits, 256, layout,
+                        tiled_nbuf(256, 256)};
     if (M % 256 == 0 && (M / 256) * cdiv(N, 128) * splits >= 256)
-        return GemmPlan{kTiled, 256, 128, 8, 2, (M / 256) * cdiv(N, 128) * splits, 512, layout};
+        return GemmPlan{kTiled, 256, 128, 8, 2, (M / 256) * cdiv(N, 128) * splits, 512, layout,
+                        tiled_nbuf(256, 128)};
     // Skinny problems.  Tile: the one that moves the fewest bytes through
     // the busiest CU.  Each workgroup streams (BM + BN) rows of its split,
     // and workgroups beyond the 256 CUs queue behind the first round.
@@ -985,6 +1000,23 @@ GemmPlan plan_gemm(int dtype, int64_t M, int64_t N, int64_t K, int64_t kps, int6
     int d = per_wave >= 2 ? 2 : 1;
     while (d > 1 && !wavek_config_exists(layout, bm, bn, w, d)) d /= 2;
     return GemmPlan{kWaveK, bm, bn, w, d, wg, w * 64, layout};
+}
+
+GemmPlan plan_gemm(int dtype, int64_t M, int64_t N, int64_t K, int64_t kps, int64_t splits,
+                   int layout) {
+    const GemmPlan p = plan_by_shape(dtype, M, N, K, kps, splits, layout);
+    // With too few 256-row tiles to fill the chip the rules above pick a
+    // skinny kernel, but where M allows 256-row tiles the large-tile kernel
+    // can still be faster on fewer CUs: each of its workgroups streams about
+    // a third of the bytes per flop.  Take whichever the cost model of the
+    // split-count choice rates faster.
+    if (p.kind != kTiled && M % 256 == 0 && getenv("SPLITK_PLAN") == nullptr) {
+        const int64_t tiles = (M / 256) * ((N + 127) / 128) * splits;
+        const GemmPlan big{kTiled, 256, 128, 8, 2, tiles, 512, layout, tiled_nbuf(256, 128)};
+        if (gemm_cost_us(big, dtype, M, N, K, kps, splits) < gemm_cost_us(p, dtype, M, N, K, kps, splits))
+            return big;
+    }
+    return p;
 }
 
 hipError_t launch_gemm_bt(const GemmPlan& plan, const void* A, const void* B, float* partials,

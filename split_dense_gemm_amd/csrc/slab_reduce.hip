@@ -125,7 +125,102 @@ hipError_t launch_out(const float* partials, void* C, int s, int64_t plane4, hip
     return launch_items<1, OT>(partials, C, s, plane4, st);
 }
 
+// Tile-ordered pass for the slabs of a skinny GEMM (BM x BN output tiles,
+// tiles_m of them down M).  Workgroup b takes tile u = xcd_logical_id(b, n):
+// the GEMM wrote every slab of tile u from the workgroups of one XCD (split
+// fastest, each XCD a contiguous range of logical ids), and when the number
+// of tiles is a multiple of 8 that XCD is the one this workgroup runs on, so
+// the slabs are still in its L2 (lines written by an XCD stay valid in its
+// L2 across the kernel boundary).  Any other count only loses locality.
+// Needs N % 4 == 0, so that 16-byte words never straddle a row or the edge
+// of a column tile.  Same arithmetic as the flat pass: ascending s, F32.
+template <int S, int BM, int BN, int OT>
+__global__ __launch_bounds__(kBlock) void slab_reduce_tiles(const float* __restrict__ P,
+                                                            void* __restrict__ C, int M, int N,
+                                                            int tiles_m) {
+    constexpr int C4 = BN / 4;               // 16-byte words per tile row
+    constexpr int ITEMS = BM * C4 / kBlock;  // words per lane
+    static_assert(ITEMS >= 1 && BM * C4 % kBlock == 0, "tile size");
+    const int u = xcd_logical_id(blockIdx.x, gridDim.x);
+    const int mt = u % tiles_m, nt = u / tiles_m;
+    const int valid4 = min(C4, (N - nt * BN) / 4);  // words of a tile row inside N
+    const int64_t plane = (int64_t)M * N;
+    const float* tile = P + (int64_t)mt * BM * N + (int64_t)nt * BN;
+    f32x4 v[ITEMS][S];
+#pragma unroll
+    for (int it = 0; it < ITEMS; ++it) {
+        const int i = threadIdx.x + it * kBlock;
+        const int row = i / C4, c4 = i % C4;
+        if (c4 < valid4) {
+#pragma unroll
+            for (int s = 0; s < S; ++s) v[it][s] = *(const f32x4*)(tile + s * plane + (int64_t)row * N + 4 * c4);
+        }
+    }
+#pragma unroll
+    for (int it = 0; it < ITEMS; ++it) {
+        const int i = threadIdx.x + it * kBlock;
+        const int row = i / C4, c4 = i % C4;
+        if (c4 < valid4) {
+            f32x4 acc = v[it][0];
+#pragma unroll
+            for (int s = 1; s < S; ++s) acc += v[it][s];
+            store4<OT>(C, (((int64_t)mt * BM + row) * N + (int64_t)nt * BN) / 4 + c4, acc);
+        }
+    }
+}
+
+template <int S, int BM, int BN, int OT>
+hipError_t launch_tiles(const float* partials, void* C, int64_t M, int64_t N, hipStream_t stream) {
+    const int tiles_m = (int)(M / BM), tiles_n = (int)((N + BN - 1) / BN);
+    int m = (int)M, n = (int)N, tm = tiles_m;
+    void* args[] = {(void*)&partials, &C, &m, &n, &tm};
+    return hipLaunchKernel((const void*)&slab_reduce_tiles<S, BM, BN, OT>,
+                           dim3((unsigned)(tiles_m * tiles_n)), dim3(kBlock), args, 0, stream);
+}
+
+template <int BM, int BN, int OT>
+hipError_t launch_tiles_s(const float* partials, void* C, int s, int64_t M, int64_t N, hipStream_t st) {
+    switch (s) {
+        case 1: return launch_tiles<1, BM, BN, OT>(partials, C, M, N, st);
+        case 2: return launch_tiles<2, BM, BN, OT>(partials, C, M, N, st);
+        case 3: return launch_tiles<3, BM, BN, OT>(partials, C, M, N, st);
+        case 4: return launch_tiles<4, BM, BN, OT>(partials, C, M, N, st);
+        case 5: return launch_tiles<5, BM, BN, OT>(partials, C, M, N, st);
+        case 6: return launch_tiles<6, BM, BN, OT>(partials, C, M, N, st);
+        case 7: return launch_tiles<7, BM, BN, OT>(partials, C, M, N, st);
+        case 8: return launch_tiles<8, BM, BN, OT>(partials, C, M, N, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <int OT>
+hipError_t launch_tiles_out(int bm, int bn, const float* partials, void* C, int s, int64_t M, int64_t N,
+                            hipStream_t st) {
+    if (bm == 32 && bn == 32) return launch_tiles_s<32, 32, OT>(partials, C, s, M, N, st);
+    if (bm == 32 && bn == 64) return launch_tiles_s<32, 64, OT>(partials, C, s, M, N, st);
+    if (bm == 64 && bn == 64) return launch_tiles_s<64, 64, OT>(partials, C, s, M, N, st);
+    return hipErrorInvalidValue;
+}
+
 }  // namespace
+
+hipError_t launch_slab_reduce_after(const GemmPlan& plan, const float* partials, void* C,
+                                    int64_t splits, int64_t M, int64_t N, int out_dtype,
+                                    hipStream_t stream) {
+    const bool skinny = plan.kind == kWaveK || plan.kind == kWaveKDma;
+    const bool tile_shape = (plan.bm == 32 && (plan.bn == 32 || plan.bn == 64)) ||
+                            (plan.bm == 64 && plan.bn == 64);
+    if (skinny && tile_shape && splits <= 8 && N % 4 == 0 && M % plan.bm == 0) {
+        const int s = (int)splits;
+        switch (out_dtype) {
+            case 0: return launch_tiles_out<0>(plan.bm, plan.bn, partials, C, s, M, N, stream);
+            case 1: return launch_tiles_out<1>(plan.bm, plan.bn, partials, C, s, M, N, stream);
+            case 2: return launch_tiles_out<2>(plan.bm, plan.bn, partials, C, s, M, N, stream);
+            default: return hipErrorInvalidValue;
+        }
+    }
+    return launch_slab_reduce(partials, C, splits, M, N, out_dtype, stream);
+}
 
 hipError_t launch_slab_reduce(const float* partials, void* C, int64_t splits, int64_t M, int64_t N,
                               int out_dtype, hipStream_t stream) {

@@ -112,7 +112,7 @@ int gemm_entry(int layout, const void* A, const void* B, float* P, void* C, int6
     const splitk::GemmPlan plan = splitk::plan_gemm(dtype, M, N, K, kps, splits, layout);
     hipError_t e = splitk::launch_gemm_bt(plan, A, B, P, M, N, K, kps, splits, dtype, (hipStream_t)stream);
     if (e != hipSuccess) return SPLITK_ERR_LAUNCH;
-    if (C) e = splitk::launch_slab_reduce(P, C, splits, M, N, out_dtype, (hipStream_t)stream);
+    if (C) e = splitk::launch_slab_reduce_after(plan, P, C, splits, M, N, out_dtype, (hipStream_t)stream);
     return e == hipSuccess ? SPLITK_OK : SPLITK_ERR_LAUNCH;
 }
 
@@ -123,8 +123,8 @@ int describe_plan(int layout, int64_t M, int64_t N, int64_t K, int64_t k_per_spl
     const splitk::GemmPlan p = splitk::plan_gemm(dtype, M, N, K, k_per_split, splits, layout);
     if (buf && len > 0) {
         if (p.kind == splitk::kTiled)
-            snprintf(buf, (size_t)len, "tiled bm%d bn%d waves%dx%d block%d grid%lld", p.bm, p.bn,
-                     p.stages, p.waves / p.stages, p.block, (long long)p.grid);
+            snprintf(buf, (size_t)len, "tiled bm%d bn%d waves%dx%d ring%d block%d grid%lld", p.bm, p.bn,
+                     p.stages, p.waves / p.stages, p.nbuf, p.block, (long long)p.grid);
         else
             snprintf(buf, (size_t)len, "%s bm%d bn%d waves%d stages%d block%d grid%lld",
                      p.kind == splitk::kWaveKDma ? "wavekdma" : "wavek", p.bm, p.bn, p.waves, p.stages,
@@ -173,6 +173,19 @@ int splitk_reduce_typed(const float* partials, void* C, int64_t splits, int64_t 
 
 int splitk_reduce(const float* partials, float* C, int64_t splits, int64_t M, int64_t N, void* stream) {
     return splitk_reduce_typed(partials, C, splits, M, N, SPLITK_F32, stream);
+}
+
+int splitk_reduce_for_gemm(const float* partials, void* C, int64_t M, int64_t N, int64_t K,
+                           int64_t k_per_split, int64_t splits, int dtype, int out_dtype,
+                           void* stream) {
+    int st = check_reduce(partials, C, splits, M, N, out_dtype);
+    if (st != SPLITK_OK) return st;
+    st = check_gemm_shape(M, N, K, k_per_split, splits, dtype);
+    if (st != SPLITK_OK) return st;
+    const splitk::GemmPlan plan = splitk::plan_gemm(dtype, M, N, K, k_per_split, splits);
+    hipError_t e = splitk::launch_slab_reduce_after(plan, partials, C, splits, M, N, out_dtype,
+                                                    (hipStream_t)stream);
+    return e == hipSuccess ? SPLITK_OK : SPLITK_ERR_LAUNCH;
 }
 
 int splitk_gemm_bt_reduce_typed(const void* A, const void* B, float* partials, void* C, int64_t M,
@@ -226,7 +239,7 @@ int splitk_gemm_bt_auto(const void* A, const void* B, float* workspace, int64_t 
     hipError_t e = splitk::launch_gemm_bt(plan, A, B, workspace, M, N, K, kps, s, dtype,
                                           (hipStream_t)stream);
     if (e != hipSuccess) return SPLITK_ERR_LAUNCH;
-    e = splitk::launch_slab_reduce(workspace, C, s, M, N, out_dtype, (hipStream_t)stream);
+    e = splitk::launch_slab_reduce_after(plan, workspace, C, s, M, N, out_dtype, (hipStream_t)stream);
     return e == hipSuccess ? SPLITK_OK : SPLITK_ERR_LAUNCH;
 }
 

@@ -27,7 +27,7 @@ def test_exports_every_declared_symbol(hip_lib):
                           "splitk_reduce_typed", "splitk_gemm_bt_reduce_typed",
                           "splitk_choose_splits", "splitk_gemm_bt_auto",
                           "splitk_gemm_bn", "splitk_gemm_bn_reduce", "splitk_describe_bn",
-                          "splitk_status_str", "splitk_describe"}
+                          "splitk_status_str", "splitk_describe", "splitk_reduce_for_gemm"}
     lib = hip_lib.load()
     for n in names:
         assert hasattr(lib, n), n

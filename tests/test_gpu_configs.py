@@ -33,7 +33,9 @@ def _configs(macro):
     text = open(SRC).read()
     body = text[text.index(f"#define {macro}(X)"):]
     body = body[: body.index("\n\n")]
-    return [tuple(int(v) for v in m) for m in re.findall(r"X\((\d+), (\d+), (\d+), (\d+)\)", body)]
+    found = [tuple(int(v) for v in m.split(",")) for m in re.findall(r"X\(([\d, ]+)\)", body)]
+    assert found, f"no configurations found for {macro}"
+    return found
 
 
 WAVEK = _configs("SPLITK_WAVEK_CONFIGS")
@@ -67,7 +69,8 @@ CASES = ([("nk", "wavek", c) for c in WAVEK] + [("nk", "wavekdma", c) for c in W
 
 
 def _plan_text(kind, cfg):
-    return f"{kind},{cfg[0]},{cfg[1]},{cfg[2]},{cfg[3]}"
+    """Override string; tiled configurations also name their ring depth."""
+    return f"{kind}," + ",".join(str(v) for v in cfg)
 
 
 def _case_id(case):
@@ -94,6 +97,8 @@ def test_override_is_honoured(hip_lib, forced):
     describe = hip_lib.describe if layout == "nk" else hip_lib.describe_bn
     text = describe(M, N, K, kps, S, 2)
     assert text.startswith(kind) and f"bm{cfg[0]} bn{cfg[1]}" in text, text
+    if kind == "tiled":
+        assert f"waves{cfg[2]}x{cfg[3]} ring{cfg[4]}" in text, text
 
 
 @pytest.mark.gpu
@@ -109,7 +114,7 @@ def test_config_parity(hip_lib, forced, dtype):
     gemm_reduce = hip_lib.gemm_bt_reduce if layout == "nk" else hip_lib.gemm_bn_reduce
     gemm = hip_lib.gemm_bt if layout == "nk" else hip_lib.gemm_bn
     dev = torch.device("cuda:0")
-    a, b = inputs.make_operands(M, N, K, dtype, seed=cfg[0] + cfg[1] + cfg[2] + cfg[3],
+    a, b = inputs.make_operands(M, N, K, dtype, seed=sum(cfg[:4]),
                                 zero_first_row=True, scale_last_row=True)
     a64 = oracle.decode(inputs.stored_bits(a), dtype)
     b64 = oracle.decode(inputs.stored_bits(b), dtype)

@@ -416,7 +416,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bt_tiled(const uint8_t* __r
                                                               const uint8_t* __restrict__ B,
                                                               float* __restrict__ P, int M, int N,
                                                               int K, int kps, int tiles_m,
-                                                              int tiles_n) {
+                                                              int tiles_n, int streaming) {
     using Op = Mfma<DT>;
     constexpr int ES = Op::kElemBytes;
     constexpr int CK = kChunkBytes / ES;
@@ -570,7 +570,19 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bt_tiled(const uint8_t* __r
     float* base = P + ((size_t)s * M + (size_t)mt * BM + wm * TM + 4 * h) * N + (size_t)nt * BN +
                   wn * TN + r;
     const int valid = N - (nt * BN + wn * TN);  // columns of this wave's sub-tile inside N
-    if (valid >= TN) {
+    // Slabs too large for the memory-side cache (stream_slabs) are stored
+    // as streaming (nontemporal) writes: they are read once, by the slab
+    // sum, and so do not displace the operands.
+    if (valid >= TN && streaming) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                float* row = base + (size_t)(mb * 32 + 8 * (i >> 2) + (i & 3)) * (size_t)N;
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) __builtin_nontemporal_store(acc[mb][nb][i], &row[nb * 32]);
+            }
+    } else if (valid >= TN) {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -602,7 +614,8 @@ hipError_t launch_tiled(const void* A, const void* B, float* P, int64_t M, int64
     const uint8_t* a = (const uint8_t*)A;
     const uint8_t* b = (const uint8_t*)B;
     int m = (int)M, n = (int)N, k = (int)K, kp = (int)kps;
-    void* args[] = {&a, &b, &P, &m, &n, &k, &kp, (void*)&tiles_m, (void*)&tiles_n};
+    int streaming = stream_slabs(splits, M, N) ? 1 : 0;
+    void* args[] = {&a, &b, &P, &m, &n, &k, &kp, (void*)&tiles_m, (void*)&tiles_n, &streaming};
     return hipLaunchKernel((const void*)&gemm_bt_tiled<DT, BM, BN, WM, WN, NBUF, BL>, grid, block, args,
                            0, stream);
 }

@@ -42,7 +42,16 @@ __device__ inline void store4(void* C, int64_t g, f32x4 v) {
     }
 }
 
-template <int S, int ITEMS, int OT>
+// Slab word load of the flat pass: streaming (nontemporal) when the slabs
+// are too large for the memory-side cache (NT, see stream_slabs), normal
+// otherwise.  Each word is read once.
+template <bool NT>
+__device__ inline f32x4 load_slab(const f32x4* p) {
+    if constexpr (NT) return __builtin_nontemporal_load(p);
+    return *p;
+}
+
+template <int S, int ITEMS, int OT, bool NT>
 __global__ __launch_bounds__(kBlock) void slab_reduce_kernel(const f32x4* __restrict__ P,
                                                              void* __restrict__ C, int splits,
                                                              int64_t plane4) {
@@ -55,7 +64,7 @@ __global__ __launch_bounds__(kBlock) void slab_reduce_kernel(const f32x4* __rest
             const int64_t g = g0 + it * stride;
             if (g < plane4) {
 #pragma unroll
-                for (int s = 0; s < S; ++s) v[it][s] = P[s * plane4 + g];
+                for (int s = 0; s < S; ++s) v[it][s] = load_slab<NT>(&P[s * plane4 + g]);
             }
         }
 #pragma unroll
@@ -75,16 +84,16 @@ __global__ __launch_bounds__(kBlock) void slab_reduce_kernel(const f32x4* __rest
         for (int it = 0; it < ITEMS; ++it) {
             const int64_t g = g0 + it * stride;
             if (g >= plane4) break;
-            f32x4 acc = P[g];
+            f32x4 acc = load_slab<NT>(&P[g]);
             int s = 1;
             for (; s + kBatch <= splits; s += kBatch) {
                 f32x4 v[kBatch];
 #pragma unroll
-                for (int j = 0; j < kBatch; ++j) v[j] = P[(int64_t)(s + j) * plane4 + g];
+                for (int j = 0; j < kBatch; ++j) v[j] = load_slab<NT>(&P[(int64_t)(s + j) * plane4 + g]);
 #pragma unroll
                 for (int j = 0; j < kBatch; ++j) acc += v[j];
             }
-            for (; s < splits; ++s) acc += P[(int64_t)s * plane4 + g];
+            for (; s < splits; ++s) acc += load_slab<NT>(&P[(int64_t)s * plane4 + g]);
             store4<OT>(C, g, acc);
         }
     }
@@ -97,8 +106,10 @@ hipError_t launch(const float* partials, void* C, int splits, int64_t plane4, hi
     const f32x4* p = (const f32x4*)partials;
     void* c = C;
     void* args[] = {&p, &c, &splits, &plane4};
-    return hipLaunchKernel((const void*)&slab_reduce_kernel<S, ITEMS, OT>, grid, dim3(kBlock), args, 0,
-                           stream);
+    const bool nt = stream_slabs(splits, 1, plane4 * 4);
+    return hipLaunchKernel(nt ? (const void*)&slab_reduce_kernel<S, ITEMS, OT, true>
+                              : (const void*)&slab_reduce_kernel<S, ITEMS, OT, false>,
+                           grid, dim3(kBlock), args, 0, stream);
 }
 
 template <int ITEMS, int OT>

@@ -43,6 +43,17 @@ __device__ inline int xcd_logical_id(int b, int n) {
     return x < r ? x * (q + 1) + slot : r * (q + 1) + (x - r) * q + slot;
 }
 
+// Slabs larger than this are written and read as streaming (nontemporal)
+// accesses.  The memory-side cache holds 256 MiB: slabs that fit stay there
+// between the GEMM and the slab sum, and normal accesses are faster
+// (2048x4096x4096 with 4 splits, 128 MiB of slabs: 3.5% slower streamed);
+// slabs that do not fit only evict the operands, and streaming them is
+// faster (2048x4096x4096 with 8 splits, 256 MiB: the chain 15% faster).
+constexpr int64_t kStreamSlabBytes = int64_t(192) << 20;
+inline bool stream_slabs(int64_t splits, int64_t M, int64_t N) {
+    return splits > 1 && splits * M * N * 4 > kStreamSlabBytes;
+}
+
 // Chooses the kernel configuration for a validated problem.
 GemmPlan plan_gemm(int dtype, int64_t M, int64_t N, int64_t K, int64_t kps, int64_t splits,
                    int layout = kLayoutNK);

@@ -328,11 +328,13 @@ def test_error_statuses_with_real_buffers(sdg):
         sdg.gemm_bt(a, b, torch.zeros(3, M, N, device=dev), kps, 3)
 
 
-@pytest.mark.parametrize("S", [2, 3, 8, 11])
-def test_reduce_alone_large_plane(sdg, S):
+@pytest.mark.parametrize("S,M,N", [(2, 2048, 2048), (3, 2048, 2048), (8, 2048, 2048), (11, 2048, 2048),
+                                   (13, 2048, 2048), (4, 4096, 4096)])
+def test_reduce_alone_large_plane(sdg, S, M, N):
     """A plane large enough for the several-words-per-lane launch: sums of
-    small integers are exact, so C must equal the reference bit for bit."""
-    M, N = 2048, 2048
+    small integers are exact, so C must equal the reference bit for bit.
+    The last two cases hold more than 192 MiB of slabs, which the pass reads
+    with streaming loads (one of them in batches of eight slabs)."""
     dev = torch.device("cuda:0")
     gen = torch.Generator().manual_seed(100 + S)
     ints = torch.randint(-1000, 1000, (S, M, N), generator=gen).float()

@@ -95,18 +95,28 @@ struct Mfma<0> {  // F32: four 32x32x2 MFMAs per 4-element piece, one element ea
 };
 
 // Output tile and split of skinny workgroup b (of n = tiles_m * tiles_n *
-// splits).  Logical ids run split fastest, then row tile, then column tile,
-// and each XCD takes a contiguous range of them: all the slabs of a tile are
-// written on one XCD, and an XCD's tiles share column panels of B.  The slab
-// sum that follows (slab_reduce_tiles) visits the tiles in the same order, so
-// that it reads the slabs from the L2 of the XCD that wrote them.
-__device__ inline void skinny_tile(int b, int n, int tiles_m, int tiles_n, int* mt, int* nt, int* s) {
-    const int splits = n / (tiles_m * tiles_n);
+// splits).  Each XCD takes a contiguous range of logical ids.
+//   order 0: row tile fastest, then column tile, then split: an XCD's
+//            workgroups share the A and B panels of one split.
+//   order 1: split fastest, then row tile, then column tile: every slab of a
+//            tile is written on one XCD, and the slab sum that follows
+//            (slab_reduce_tiles) visits the tiles in the same order, reading
+//            the slabs from the L2 of the XCD that wrote them.  It costs the
+//            GEMM the whole K range of fewer tiles per XCD, so the planner
+//            takes it only where that still fits the XCD's L2.
+struct TileId {
+    int mt, nt, s;  // row tile, column tile, split
+};
+__device__ __attribute__((always_inline)) inline TileId skinny_tile(int b, int n, int tiles_m,
+                                                                    int tiles_n, int order) {
     const int logical = xcd_logical_id(b, n);
-    *s = logical % splits;
-    const int u = logical / splits;
-    *mt = u % tiles_m;
-    *nt = u / tiles_m;
+    if (order == 1) {
+        const int splits = n / (tiles_m * tiles_n);
+        const int u = logical / splits;
+        return TileId{u % tiles_m, u / tiles_m, logical % splits};
+    }
+    const int rest = logical / tiles_m;
+    return TileId{logical % tiles_m, rest % tiles_n, rest / tiles_n};
 }
 
 // LDS slot of 16-byte piece p of staged row r.  XOR-swizzled so that the
@@ -242,7 +252,7 @@ template <int DT, int BM, int BN, int W, int D, int BL>
 __global__ __launch_bounds__(W * 64) void gemm_bt_wavek(const uint8_t* __restrict__ A,
                                                         const uint8_t* __restrict__ B,
                                                         float* __restrict__ P, int M, int N, int K,
-                                                        int kps, int tiles_m, int tiles_n) {
+                                                        int kps, int tiles_m, int tiles_n, int order) {
     using Op = Mfma<DT>;
     constexpr int ES = Op::kElemBytes;
     constexpr int CK = kChunkBytes / ES;  // elements per chunk
@@ -256,8 +266,8 @@ __global__ __launch_bounds__(W * 64) void gemm_bt_wavek(const uint8_t* __restric
     constexpr int RED_BYTES = W * BN * (BM + 4) * 4;  // sum_and_store's tiles
     __shared__ __attribute__((aligned(16))) uint8_t smem[STAGE_BYTES > RED_BYTES ? STAGE_BYTES : RED_BYTES];
 
-    int mt, nt, s;
-    skinny_tile(blockIdx.x, gridDim.x, tiles_m, tiles_n, &mt, &nt, &s);
+    const TileId tile = skinny_tile(blockIdx.x, gridDim.x, tiles_m, tiles_n, order);
+    const int mt = tile.mt, nt = tile.nt, s = tile.s;
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -648,7 +658,7 @@ __global__ __launch_bounds__(W * 64) void gemm_bt_wavek_dma(const uint8_t* __res
                                                             const uint8_t* __restrict__ B,
                                                             float* __restrict__ P, int M, int N,
                                                             int K, int kps, int tiles_m,
-                                                            int tiles_n) {
+                                                            int tiles_n, int order) {
     using Op = Mfma<DT>;
     constexpr int ES = Op::kElemBytes;
     constexpr int CK = kChunkBytes / ES;
@@ -665,8 +675,8 @@ __global__ __launch_bounds__(W * 64) void gemm_bt_wavek_dma(const uint8_t* __res
     __shared__ __attribute__((aligned(16))) uint8_t tr_lds[W][BLOCK];
     __shared__ __attribute__((aligned(16))) uint8_t dma_lds[W][ROWS * kChunkBytes];
 
-    int mt, nt, s;
-    skinny_tile(blockIdx.x, gridDim.x, tiles_m, tiles_n, &mt, &nt, &s);
+    const TileId tile = skinny_tile(blockIdx.x, gridDim.x, tiles_m, tiles_n, order);
+    const int mt = tile.mt, nt = tile.nt, s = tile.s;
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -787,27 +797,27 @@ __global__ __launch_bounds__(W * 64) void gemm_bt_wavek_dma(const uint8_t* __res
 
 template <int DT, int BM, int BN, int W, int R>
 hipError_t launch_wavek_dma(const void* A, const void* B, float* P, int64_t M, int64_t N, int64_t K,
-                            int64_t kps, int64_t splits, hipStream_t stream) {
+                            int64_t kps, int64_t splits, int order, hipStream_t stream) {
     const int tiles_m = (int)(M / BM), tiles_n = (int)((N + BN - 1) / BN);
     const dim3 grid((unsigned)(tiles_m * (int64_t)tiles_n * splits));
     const uint8_t* a = (const uint8_t*)A;
     const uint8_t* b = (const uint8_t*)B;
     int m = (int)M, n = (int)N, k = (int)K, kp = (int)kps;
-    void* args[] = {&a, &b, &P, &m, &n, &k, &kp, (void*)&tiles_m, (void*)&tiles_n};
+    void* args[] = {&a, &b, &P, &m, &n, &k, &kp, (void*)&tiles_m, (void*)&tiles_n, &order};
     return hipLaunchKernel((const void*)&gemm_bt_wavek_dma<DT, BM, BN, W, R>, grid, dim3(W * 64), args,
                            0, stream);
 }
 
 template <int DT, int BM, int BN, int W, int D, int BL>
 hipError_t launch_wavek(const void* A, const void* B, float* P, int64_t M, int64_t N, int64_t K,
-                        int64_t kps, int64_t splits, hipStream_t stream) {
+                        int64_t kps, int64_t splits, int order, hipStream_t stream) {
     const int tiles_m = (int)(M / BM), tiles_n = (int)((N + BN - 1) / BN);
     const dim3 grid((unsigned)(tiles_m * (int64_t)tiles_n * splits));
     const dim3 block(W * 64);
     const uint8_t* a = (const uint8_t*)A;
     const uint8_t* b = (const uint8_t*)B;
     int m = (int)M, n = (int)N, k = (int)K, kp = (int)kps;
-    void* args[] = {&a, &b, &P, &m, &n, &k, &kp, (void*)&tiles_m, (void*)&tiles_n};
+    void* args[] = {&a, &b, &P, &m, &n, &k, &kp, (void*)&tiles_m, (void*)&tiles_n, &order};
     return hipLaunchKernel((const void*)&gemm_bt_wavek<DT, BM, BN, W, D, BL>, grid, block, args, 0,
                            stream);
 }
@@ -855,7 +865,7 @@ hipError_t launch_dtype_kn(const GemmPlan& p, const void* A, const void* B, floa
     if (p.kind == kWaveK) {
 #define X(cbm, cbn, cw, cd)                                                    \
     if (p.bm == cbm && p.bn == cbn && p.waves == cw && p.stages == cd)        \
-        return launch_wavek<DT, cbm, cbn, cw, cd, 1>(A, B, P, M, N, K, kps, splits, st);
+        return launch_wavek<DT, cbm, cbn, cw, cd, 1>(A, B, P, M, N, K, kps, splits, p.order, st);
         SPLITK_KN_WAVEK_CONFIGS(X)
 #undef X
     }
@@ -877,14 +887,14 @@ hipError_t launch_dtype(const GemmPlan& p, const void* A, const void* B, float* 
     if (p.kind == kWaveK) {
 #define X(cbm, cbn, cw, cd)                                                    \
     if (p.bm == cbm && p.bn == cbn && p.waves == cw && p.stages == cd)        \
-        return launch_wavek<DT, cbm, cbn, cw, cd, 0>(A, B, P, M, N, K, kps, splits, st);
+        return launch_wavek<DT, cbm, cbn, cw, cd, 0>(A, B, P, M, N, K, kps, splits, p.order, st);
         SPLITK_WAVEK_CONFIGS(X)
 #undef X
     }
     if (p.kind == kWaveKDma) {
 #define X(cbm, cbn, cw, cr)                                                     \
     if (p.bm == cbm && p.bn == cbn && p.waves == cw && p.stages == cr)          \
-        return launch_wavek_dma<DT, cbm, cbn, cw, cr>(A, B, P, M, N, K, kps, splits, st);
+        return launch_wavek_dma<DT, cbm, cbn, cw, cr>(A, B, P, M, N, K, kps, splits, p.order, st);
         SPLITK_WAVEKDMA_CONFIGS(X)
 #undef X
     }
@@ -1015,9 +1025,31 @@ static GemmPlan plan_by_shape(int dtype, int64_t M, int64_t N, int64_t K, int64_
     return GemmPlan{kWaveK, bm, bn, w, d, wg, w * 64, layout};
 }
 
+// Operand bytes one XCD may stream for the tiles it holds at once under the
+// split-fastest order (order 1): past this the K range of those tiles
+// crowds the 4 MiB L2.  Measured: 1.5 MiB (256x1024x2048, 2 splits) and
+// 2.25 MiB (512x1024x2048, 2 splits) gain 0.35 and 1.3 us per GEMM + slab
+// sum; 4.5 MiB (64x768x12288, 8 splits; 192x768x6144, 2 splits) and more
+// lost 0.4-11 us, the GEMM slowing by up to 27%.
+constexpr int64_t kSplitFastBytes = int64_t(3) << 20;
+
+// Tile order of a plan: split fastest where the tile-ordered slab sum
+// applies (a skinny tile of 32x32, 32x64 or 64x64, 2..8 splits, N % 4 == 0)
+// and the operand panels of the tiles on one XCD fit kSplitFastBytes.
+static int tile_order(const GemmPlan& p, int dtype, int64_t M, int64_t N, int64_t K, int64_t splits) {
+    if (p.kind == kTiled || splits < 2 || splits > 8 || N % 4 != 0) return 0;
+    if (!((p.bm == 32 && (p.bn == 32 || p.bn == 64)) || (p.bm == 64 && p.bn == 64))) return 0;
+    const int64_t es = dtype == 0 ? 4 : 2;
+    const int64_t tiles_m = M / p.bm;
+    const int64_t held = 32 / splits > 1 ? 32 / splits : 1;  // tiles per XCD at once, one workgroup per CU
+    const int64_t rows = (held < tiles_m ? held : tiles_m) * p.bm + ((held + tiles_m - 1) / tiles_m) * p.bn;
+    return rows * K * es <= kSplitFastBytes ? 1 : 0;
+}
+
 GemmPlan plan_gemm(int dtype, int64_t M, int64_t N, int64_t K, int64_t kps, int64_t splits,
                    int layout) {
-    const GemmPlan p = plan_by_shape(dtype, M, N, K, kps, splits, layout);
+    GemmPlan p = plan_by_shape(dtype, M, N, K, kps, splits, layout);
+    p.order = tile_order(p, dtype, M, N, K, splits);
     // With too few 256-row tiles to fill the chip the rules above pick a
     // skinny kernel, but where M allows 256-row tiles the large-tile kernel
     // can still be faster on fewer CUs: each of its workgroups streams about

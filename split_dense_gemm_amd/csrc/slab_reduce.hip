@@ -218,10 +218,9 @@ hipError_t launch_tiles_out(int bm, int bn, const float* partials, void* C, int 
 hipError_t launch_slab_reduce_after(const GemmPlan& plan, const float* partials, void* C,
                                     int64_t splits, int64_t M, int64_t N, int out_dtype,
                                     hipStream_t stream) {
-    const bool skinny = plan.kind == kWaveK || plan.kind == kWaveKDma;
     const bool tile_shape = (plan.bm == 32 && (plan.bn == 32 || plan.bn == 64)) ||
                             (plan.bm == 64 && plan.bn == 64);
-    if (skinny && tile_shape && splits <= 8 && N % 4 == 0 && M % plan.bm == 0) {
+    if (plan.order == 1 && tile_shape && splits <= 8 && N % 4 == 0 && M % plan.bm == 0) {
         const int s = (int)splits;
         switch (out_dtype) {
             case 0: return launch_tiles_out<0>(plan.bm, plan.bn, partials, C, s, M, N, stream);

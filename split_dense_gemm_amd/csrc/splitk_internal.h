@@ -32,12 +32,13 @@ struct GemmPlan {
     int block;     // threads per workgroup
     int layout;    // BLayout of B
     int nbuf = 0;  // tiled kernels: chunk buffers in the LDS ring (0: the tile's default)
+    int order = 0; // skinny kernels: 1 = splits of a tile on one XCD (see skinny_tile)
 };
 
 // Renumbers workgroups so that consecutive logical ids run on one XCD.
 // Workgroup b is dispatched to XCD b % 8; logical ids [start_x, start_x+cnt_x)
 // go to XCD x.  It is a bijection on [0, n) whatever the dispatch order.
-__device__ inline int xcd_logical_id(int b, int n) {
+__device__ __attribute__((always_inline)) inline int xcd_logical_id(int b, int n) {
     const int q = n >> 3, r = n & 7;
     const int x = b & 7, slot = b >> 3;
     return x < r ? x * (q + 1) + slot : r * (q + 1) + (x - r) * q + slot;
@@ -66,10 +67,10 @@ hipError_t launch_gemm_bt(const GemmPlan& plan, const void* A, const void* B, fl
 hipError_t launch_slab_reduce(const float* partials, void* C, int64_t splits, int64_t M, int64_t N,
                               int out_dtype, hipStream_t stream);
 
-// The same sum for slabs that the GEMM `plan` has just written: for the
-// skinny kernels each workgroup takes one output tile, on the XCD whose L2
-// holds that tile's slabs; otherwise (and where that order does not apply)
-// the flat pass above.
+// The same sum for slabs that the GEMM `plan` has just written: after a
+// skinny GEMM in the split-fastest order (plan.order == 1) each workgroup
+// takes one output tile, on the XCD whose L2 holds that tile's slabs;
+// otherwise the flat pass above.
 hipError_t launch_slab_reduce_after(const GemmPlan& plan, const float* partials, void* C,
                                     int64_t splits, int64_t M, int64_t N, int out_dtype,
                                     hipStream_t stream);

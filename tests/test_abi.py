@@ -240,7 +240,23 @@ def test_tail_tiles_in_plans(hip_lib):
     text = hip_lib.describe(2048, 4000, 1024, 256, 4, BF16)
     assert text.startswith("tiled bm256 bn128") and text.endswith(f"grid{8 * 32 * 4}"), text
     text = hip_lib.describe(64, 100, 1024, 256, 4, BF16)
-    assert text.endswith("grid" + str(2 * (2 if " bn64 " in text else 4) * 4)), text
+    assert f" grid{2 * (2 if ' bn64 ' in text else 4) * 4}" in text, text
+
+
+def test_tile_order_choice(hip_lib):
+    """Skinny plans put every split of a tile on one XCD ("splitfast") only
+    while the operand panels of the tiles one XCD holds at once stay within
+    3 MiB of its L2; large tiles, long K and shapes the tile-ordered slab sum
+    cannot serve (N % 4 != 0, more than eight splits) keep the split-major
+    order."""
+    fast = [(256, 1024, 2048, 1024, 2), (512, 1024, 2048, 1024, 2), (96, 512, 2048, 512, 4),
+            (64, 256, 2048, 256, 8)]
+    major = [(64, 768, 12288, 1536, 8), (192, 768, 6144, 3072, 2), (192, 3072, 12288, 3072, 4),
+             (64, 130, 512, 256, 2), (32, 64, 2048, 128, 16), (2048, 4096, 4096, 512, 8)]
+    for shape in fast:
+        assert hip_lib.describe(*shape, BF16).endswith(" splitfast"), shape
+    for shape in major:
+        assert "splitfast" not in hip_lib.describe(*shape, BF16), shape
 
 
 @pytest.mark.parametrize("args,status", SHAPE_CASES)

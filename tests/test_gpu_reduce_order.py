@@ -29,19 +29,20 @@ GUARD_BITS = np.float32(inputs.GUARD_VALUE).view(np.uint32)
 GUARD16 = {d: int(inputs.stored_bits(torch.tensor([inputs.GUARD_VALUE], dtype=inputs.DTYPES[d]))[0])
            for d in ("f16", "bf16")}
 
-# (M, N, K, k_per_split, splits, input dtype, forced plan or None)
+# (M, N, K, k_per_split, splits, input dtype, forced plan or None, tile order expected)
 GEOMETRIES = [
-    (256, 1024, 2048, 1024, 2, "bf16", None),    # 32x64 tiles, 128 of them
-    (96, 512, 2048, 512, 4, "bf16", None),       # 32x32 tiles, 48
-    (32, 512, 2080, 544, 4, "f16", None),        # 32x32, 16 tiles, short last split
-    (96, 320, 1024, 256, 4, "bf16", None),       # 30 tiles: not a multiple of 8
-    (96, 200, 1024, 512, 2, "bf16", None),       # column tail (N % 4 == 0)
-    (64, 100, 512, 256, 2, "f32", None),         # F32 plan, column tail
-    (64, 256, 2048, 256, 8, "bf16", None),       # eight slabs (largest tile-order count)
-    (128, 256, 1024, 512, 2, "bf16", "wavek,64,64,4,2"),   # forced 64x64 tiles
-    (64, 130, 512, 256, 2, "bf16", None),        # N % 4 != 0: flat order
-    (32, 64, 2048, 128, 16, "bf16", None),       # sixteen slabs: flat order
-    (2048, 2048, 1024, 512, 2, "bf16", None),    # large-tile GEMM: flat order
+    (256, 1024, 2048, 1024, 2, "bf16", None, True),    # 32x64 tiles, 128 of them
+    (96, 512, 2048, 512, 4, "bf16", None, True),       # 32x32 tiles, 48
+    (32, 512, 2080, 544, 4, "f16", None, True),        # 32x32, 16 tiles, short last split
+    (96, 320, 1024, 256, 4, "bf16", None, True),       # 30 tiles: not a multiple of 8
+    (96, 200, 1024, 512, 2, "bf16", None, True),       # column tail (N % 4 == 0)
+    (64, 100, 512, 256, 2, "f32", None, True),         # F32 plan, column tail
+    (64, 256, 2048, 256, 8, "bf16", None, True),       # eight slabs (largest tile-order count)
+    (128, 256, 1024, 512, 2, "bf16", "wavek,64,64,4,2", True),   # forced 64x64 tiles
+    (64, 768, 12288, 1536, 8, "bf16", None, False),    # long K: split-major order, flat pass
+    (64, 130, 512, 256, 2, "bf16", None, False),       # N % 4 != 0: flat order
+    (32, 64, 2048, 128, 16, "bf16", None, False),      # sixteen slabs: flat order
+    (2048, 2048, 1024, 512, 2, "bf16", None, False),   # large-tile GEMM: flat order
 ]
 
 
@@ -83,13 +84,14 @@ def _run(sdg, fn_name, slabs, M, N, geo, out):
 
 @pytest.mark.parametrize("out", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("geo", GEOMETRIES, ids=lambda g: "x".join(map(str, g[:5])) + f"-{g[5]}"
-                         + ("-forced" if g[6] else ""))
+                         + ("-forced" if g[6] else "") + ("-tiles" if g[7] else "-flat"))
 def test_tile_order_equals_flat_order(sdg, plan_env, geo, out):
-    M, N, K, kps, S, dt, plan = geo
+    M, N, K, kps, S, dt, plan, tile_order = geo
     if plan:
         os.environ["SPLITK_PLAN"] = plan
-    print(f"reduce order: {geo} out={out} plan={sdg.describe(M, N, K, kps, S, inputs.DTYPES[dt])}",
-          flush=True)
+    text = sdg.describe(M, N, K, kps, S, inputs.DTYPES[dt])
+    print(f"reduce order: {geo} out={out} plan={text}", flush=True)
+    assert ("splitfast" in text) == tile_order, text
     slabs = _slabs(M, N, S, seed=M + N + S)
     got = _run(sdg, "tile", slabs, M, N, geo, out)
     flat = _run(sdg, "flat", slabs, M, N, geo, out)

@@ -492,16 +492,16 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bt_tiled(const uint8_t* __r
                      (size_t)k0 * ES;
         }
     }
-    // Chunk c into ring slot c % NBUF.  In a half chunk the lanes meant for
-    // pieces 4..7 re-read pieces 0..3 (in bounds); those copies are finite
-    // and meet zero A fragments in compute().
-    auto dma = [&](int c) {
+    // DMA instructions [lo, hi) of chunk c, into ring slot c % NBUF.  In a
+    // half chunk the lanes meant for pieces 4..7 re-read pieces 0..3 (in
+    // bounds); those copies are finite and meet zero A fragments in compute().
+    auto dma = [&](int c, int lo, int hi) {
         uint8_t* buf = smem + (c % NBUF) * BUF;
         const bool half = half_chunk(c);
         const int mask = half ? 3 : 7;
         const size_t off = (size_t)c * kChunkBytes;
 #pragma unroll
-        for (int i = 0; i < DPW; ++i) {
+        for (int i = lo; i < hi; ++i) {
             const uint8_t* g;
             if (BL == 1 && i >= IA) {
                 // B as [K,N]: in a half chunk the second half of the k-rows
@@ -523,7 +523,12 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bt_tiled(const uint8_t* __r
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x16{};
 
-    auto compute = [&](int c) {
+    // MFMA work of chunk c.  When `next` >= 0, the DMA of chunk `next` is
+    // issued a quarter after each of the four k-steps: issued all at once,
+    // the wave stalled ~1200 cycles per chunk waiting for the texture path to
+    // accept it, with no MFMA in flight (measured on 256x256 tiles; spread,
+    // the chunk's work went from ~4100 to ~3550 cycles).
+    auto compute = [&](int c, int next) {
         const uint8_t* lds = smem + (c % NBUF) * BUF;
         const int steps = half_chunk(c) ? 2 : 4;
 #pragma unroll
@@ -551,27 +556,27 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bt_tiled(const uint8_t* __r
 #pragma unroll
                     for (int nb = 0; nb < NB; ++nb)
                         acc[mb][nb] = Op::step(fa[mb], fb[nb], acc[mb][nb], e);
+            if (next >= 0) dma(next, q * DPW / 4, (q + 1) * DPW / 4);
         }
     };
 
     // Prologue: the first NBUF - 1 chunks in flight.
 #pragma unroll
     for (int j = 0; j < NBUF - 1; ++j)
-        if (j < nchunks) dma(j);
+        if (j < nchunks) dma(j, 0, DPW);
     // Steady state: every pass issues one more chunk, so exactly NBUF - 2
     // younger chunks (DPW loads each) are outstanding behind chunk c.
     int c = 0;
     for (; c + NBUF - 1 < nchunks; ++c) {
         __builtin_amdgcn_s_waitcnt(SPLITK_VMCNT((NBUF - 2) * DPW));
         lds_barrier();  // chunk c complete for all waves; slot of chunk c-1 free
-        dma(c + NBUF - 1);
-        compute(c);
+        compute(c, c + NBUF - 1);
     }
     // Tail: no more loads to issue; wait for everything still in flight.
     for (; c < nchunks; ++c) {
         __builtin_amdgcn_s_waitcnt(SPLITK_VMCNT(0));
         lds_barrier();
-        compute(c);
+        compute(c, -1);
     }
 
     // Register i of lane l holds row 8*(i/4) + 4*(l/32) + i%4, column l%32.

@@ -170,20 +170,24 @@ __device__ inline size_t kn_src(int u, int j, size_t row_bytes_b, size_t col0) {
 
 // Cross-wave sum of a skinny workgroup's W partial BM x BN tiles, and its
 // store.  Each wave writes its accumulators column-major into its own LDS
-// tile: the four registers 4g..4g+3 of a 32x32 block hold four consecutive
-// rows of one column, so each group is one 16-byte write.  A column pitch of
-// BM + 4 floats steps 16 bytes further round the banks per column, which
-// keeps the lanes of a write (and of the reads below) on distinct banks.  Then
-// each thread takes one column and four rows, adds the W tiles in ascending
-// wave order and stores the four values.  Consecutive lanes hold consecutive
+// tile (wave w's tile starts TS floats after wave w-1's): the four
+// registers 4g..4g+3 of a 32x32 block hold four consecutive rows of one
+// column, so each group is one 16-byte write.  A column pitch of BM + 4
+// floats steps 16 bytes further round the banks per column, which keeps the
+// lanes of a write (and of the reads below) on distinct banks.  Then each
+// thread takes one column and four rows, adds the W tiles in ascending wave
+// order and stores the four values.  Consecutive lanes hold consecutive
 // columns, so every store instruction writes whole row segments; columns at
-// or past `valid` (outside N) are not stored.  The caller has made the LDS
-// area free (a barrier after its last use).
-template <int BM, int BN, int W, int MB, int NB>
+// or past `valid` (outside N) are not stored.  The caller guarantees that no
+// other wave still reads a wave's tile area when that wave calls this: its
+// own staging area (TS floats per wave, reused), or an area freed by a
+// barrier.
+template <int BM, int BN, int W, int MB, int NB, int TS>
 __device__ inline void sum_and_store(float* lds, const f32x16 (&acc)[MB][NB], float* out, int N,
                                      int valid, int wave, int lane) {
     constexpr int CP = BM + 4;  // floats per column of one wave's tile
-    float* mine = lds + wave * BN * CP;
+    static_assert(TS >= BN * CP, "tile stride");
+    float* mine = lds + wave * TS;
     const int r = lane & 31, h = lane >> 5;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
@@ -200,7 +204,7 @@ __device__ inline void sum_and_store(float* lds, const f32x16 (&acc)[MB][NB], fl
         const int col = it % BN, rq = it / BN;
         f32x4 v = *(const f32x4*)(lds + col * CP + 4 * rq);
 #pragma unroll
-        for (int w = 1; w < W; ++w) v += *(const f32x4*)(lds + (w * BN + col) * CP + 4 * rq);
+        for (int w = 1; w < W; ++w) v += *(const f32x4*)(lds + w * TS + col * CP + 4 * rq);
         if (col < valid) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) out[(size_t)(4 * rq + e) * N + col] = v[e];
@@ -263,6 +267,10 @@ __global__ __launch_bounds__(W * 64) void gemm_bt_wavek(const uint8_t* __restric
     // One LDS block: per-wave staging buffers during the k loop, then (after
     // a barrier) the W partial tiles of the cross-wave sum.
     constexpr int STAGE_BYTES = W * ROWS * kChunkBytes;
+    // Each wave's partial tile goes into its own staging area when it fits
+    // there (no barrier needed first); otherwise all tiles go at the front
+    // once every wave is done staging.
+    constexpr bool OWN = BN * (BM + 4) * 4 <= ROWS * kChunkBytes;
     constexpr int RED_BYTES = W * BN * (BM + 4) * 4;  // sum_and_store's tiles
     __shared__ __attribute__((aligned(16))) uint8_t smem[STAGE_BYTES > RED_BYTES ? STAGE_BYTES : RED_BYTES];
 
@@ -392,8 +400,9 @@ __global__ __launch_bounds__(W * 64) void gemm_bt_wavek(const uint8_t* __restric
     for (int j = 0; j < D; ++j)
         if (t + j < mine) compute(chunk_of(t + j), stg[j]);
 
-    __syncthreads();  // every wave is done with its staging buffer
-    sum_and_store<BM, BN, W, MB, NB>(reinterpret_cast<float*>(smem), acc,
+    if constexpr (!OWN) __syncthreads();  // every wave is done with its staging buffer
+    sum_and_store<BM, BN, W, MB, NB, OWN ? ROWS * kChunkBytes / 4 : BN * (BM + 4)>(
+        reinterpret_cast<float*>(smem), acc,
                                      P + ((size_t)s * M + (size_t)mt * BM) * N + (size_t)nt * BN, N,
                                      min(BN, N - nt * BN), wave, lane);
 }
@@ -672,11 +681,11 @@ __global__ __launch_bounds__(W * 64) void gemm_bt_wavek_dma(const uint8_t* __res
     constexpr int LOADS = ROWS / 8;
     constexpr int BLOCK = 32 * kChunkBytes;          // one 32-row block of a chunk
     static_assert(LOADS < 64 && R * LOADS + LOADS < 64, "vmcnt range");
-    static_assert(W * BN * (BM + 4) * 4 <= W * ROWS * kChunkBytes, "reduction tiles fit the DMA area");
+    static_assert(BN * (BM + 4) * 4 <= ROWS * kChunkBytes, "a wave's reduction tile fits its DMA area");
     // Separate LDS objects for the transpose blocks and the DMA chunks, so
     // the compiler can see that writing a transpose block does not have to
-    // wait for the DMA still in flight.  The reduction tile reuses the DMA
-    // area after a barrier.
+    // wait for the DMA still in flight.  Each wave's reduction tile reuses
+    // that wave's own DMA area.
     __shared__ __attribute__((aligned(16))) uint8_t tr_lds[W][BLOCK];
     __shared__ __attribute__((aligned(16))) uint8_t dma_lds[W][ROWS * kChunkBytes];
 
@@ -794,8 +803,10 @@ __global__ __launch_bounds__(W * 64) void gemm_bt_wavek_dma(const uint8_t* __res
         mfma_chunk(fa, fb, chunk_of(mine - 1));
     }
 
-    __syncthreads();  // every wave is done with its LDS areas
-    sum_and_store<BM, BN, W, MB, NB>(reinterpret_cast<float*>(&dma_lds[0][0]), acc,
+    // The partial tile goes into this wave's own DMA area, which no other
+    // wave reads: no barrier before the writes, so early waves write while
+    // late ones still multiply (measured ~0.3 us off the headline GEMM).
+    sum_and_store<BM, BN, W, MB, NB, ROWS * kChunkBytes / 4>(reinterpret_cast<float*>(&dma_lds[0][0]), acc,
                                      P + ((size_t)s * M + (size_t)mt * BM) * N + (size_t)nt * BN, N,
                                      min(BN, N - nt * BN), wave, lane);
 }

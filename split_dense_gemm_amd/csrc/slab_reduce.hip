@@ -136,8 +136,13 @@ hipError_t launch_out(const float* partials, void* C, int s, int64_t plane4, hip
     return launch_items<1, OT>(partials, C, s, plane4, st);
 }
 
+// Row bands per tile in the tile-ordered pass: one 16-byte word per lane.
+constexpr int tile_bands(int bm, int bn) { return bm * bn / (4 * kBlock) > 1 ? bm * bn / (4 * kBlock) : 1; }
+
 // Tile-ordered pass for the slabs of a skinny GEMM (BM x BN output tiles,
-// tiles_m of them down M).  Workgroup b takes tile u = xcd_logical_id(b, n):
+// tiles_m of them down M).  Each tile is split into PT row bands of one
+// 16-byte word per lane; workgroup b takes band lr % PT of tile
+// u = lr / PT, lr = xcd_logical_id(b, n):
 // the GEMM wrote every slab of tile u from the workgroups of one XCD (split
 // fastest, each XCD a contiguous range of logical ids), and when the number
 // of tiles is a multiple of 8 that XCD is the one this workgroup runs on, so
@@ -149,14 +154,16 @@ template <int S, int BM, int BN, int OT>
 __global__ __launch_bounds__(kBlock) void slab_reduce_tiles(const float* __restrict__ P,
                                                             void* __restrict__ C, int M, int N,
                                                             int tiles_m) {
-    constexpr int C4 = BN / 4;               // 16-byte words per tile row
-    constexpr int ITEMS = BM * C4 / kBlock;  // words per lane
-    static_assert(ITEMS >= 1 && BM * C4 % kBlock == 0, "tile size");
-    const int u = xcd_logical_id(blockIdx.x, gridDim.x);
+    constexpr int C4 = BN / 4;                  // 16-byte words per tile row
+    constexpr int PT = tile_bands(BM, BN);      // workgroups per tile
+    constexpr int ITEMS = BM * C4 / PT / kBlock;  // words per lane
+    static_assert(ITEMS >= 1 && BM * C4 % (PT * kBlock) == 0, "tile size");
+    const int lr = xcd_logical_id(blockIdx.x, gridDim.x);
+    const int u = lr / PT, band = lr % PT;
     const int mt = u % tiles_m, nt = u / tiles_m;
     const int valid4 = min(C4, (N - nt * BN) / 4);  // words of a tile row inside N
     const int64_t plane = (int64_t)M * N;
-    const float* tile = P + (int64_t)mt * BM * N + (int64_t)nt * BN;
+    const float* tile = P + ((int64_t)mt * BM + band * (BM / PT)) * N + (int64_t)nt * BN;
     f32x4 v[ITEMS][S];
 #pragma unroll
     for (int it = 0; it < ITEMS; ++it) {
@@ -175,7 +182,7 @@ __global__ __launch_bounds__(kBlock) void slab_reduce_tiles(const float* __restr
             f32x4 acc = v[it][0];
 #pragma unroll
             for (int s = 1; s < S; ++s) acc += v[it][s];
-            store4<OT>(C, (((int64_t)mt * BM + row) * N + (int64_t)nt * BN) / 4 + c4, acc);
+            store4<OT>(C, (((int64_t)mt * BM + band * (BM / PT) + row) * N + (int64_t)nt * BN) / 4 + c4, acc);
         }
     }
 }
@@ -186,7 +193,8 @@ hipError_t launch_tiles(const float* partials, void* C, int64_t M, int64_t N, hi
     int m = (int)M, n = (int)N, tm = tiles_m;
     void* args[] = {(void*)&partials, &C, &m, &n, &tm};
     return hipLaunchKernel((const void*)&slab_reduce_tiles<S, BM, BN, OT>,
-                           dim3((unsigned)(tiles_m * tiles_n)), dim3(kBlock), args, 0, stream);
+                           dim3((unsigned)(tiles_m * tiles_n * tile_bands(BM, BN))), dim3(kBlock), args, 0,
+                           stream);
 }
 
 template <int BM, int BN, int OT>

@@ -37,7 +37,11 @@
 //    N re-read row N-1 (or, for [K,N], the row's last 16 bytes) and its
 //    output columns past N are never stored.
 //  * Workgroups are renumbered so that the tiles sharing operand panels run
-//    on one XCD and reuse them from that XCD's L2.
+//    on one XCD and reuse them from that XCD's L2.  Where it fits the L2,
+//    the skinny kernels instead put every split of a tile on one XCD, so
+//    that the slab sum can read the slabs from the L2 that holds them.
+//  * Slabs too large for the memory-side cache are stored as streaming
+//    writes (stream_slabs).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdio.h>

@@ -48,6 +48,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "splitk_internal.h"
 
 namespace splitk {
@@ -439,7 +441,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bt_tiled(const uint8_t* __r
                                                               const uint8_t* __restrict__ B,
                                                               float* __restrict__ P, int M, int N,
                                                               int K, int kps, int tiles_m,
-                                                              int tiles_n, int streaming) {
+                                                              int tiles_n, int streaming,
+                                                              int stagger) {
     using Op = Mfma<DT>;
     constexpr int ES = Op::kElemBytes;
     constexpr int CK = kChunkBytes / ES;
@@ -577,6 +580,16 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bt_tiled(const uint8_t* __r
 #pragma unroll
     for (int j = 0; j < NBUF - 1; ++j)
         if (j < nchunks) dma(j, 0, DPW);
+    // Staggered start.  On a grid of several rounds the CUs would otherwise
+    // run in lockstep: all of them store their partial tiles at the same
+    // moment, each at 1/256 of the write bandwidth while no MFMA work runs
+    // anywhere.  The first round's workgroups (one per CU) wait 512 cycles
+    // per slot of their XCD, 0 to 31 slots, once their first chunks are in
+    // flight, which spreads the store phases over about one tile's store time.
+    if ((int)blockIdx.x < stagger) {
+        const int slot = (blockIdx.x >> 3) & 31;
+        for (int i = 0; i < slot; ++i) __builtin_amdgcn_s_sleep(8);
+    }
     // Steady state: every pass issues one more chunk, so exactly NBUF - 2
     // younger chunks (DPW loads each) are outstanding behind chunk c.
     int c = 0;
@@ -633,6 +646,20 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bt_tiled(const uint8_t* __r
     }
 }
 
+// Compute units of the current device, looked up once per device.
+int device_cus() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
 template <int DT, int BM, int BN, int WM, int WN, int NBUF, int BL>
 hipError_t launch_tiled(const void* A, const void* B, float* P, int64_t M, int64_t N, int64_t K,
                         int64_t kps, int64_t splits, hipStream_t stream) {
@@ -643,7 +670,11 @@ hipError_t launch_tiled(const void* A, const void* B, float* P, int64_t M, int64
     const uint8_t* b = (const uint8_t*)B;
     int m = (int)M, n = (int)N, k = (int)K, kp = (int)kps;
     int streaming = stream_slabs(splits, M, N) ? 1 : 0;
-    void* args[] = {&a, &b, &P, &m, &n, &k, &kp, (void*)&tiles_m, (void*)&tiles_n, &streaming};
+    // Every instantiated tile needs a whole CU (LDS ring of 128-144 KiB), so
+    // the first device_cus() workgroups are the first round.
+    const int cus = device_cus();
+    int stagger = (int64_t)grid.x > cus ? cus : 0;
+    void* args[] = {&a, &b, &P, &m, &n, &k, &kp, (void*)&tiles_m, (void*)&tiles_n, &streaming, &stagger};
     return hipLaunchKernel((const void*)&gemm_bt_tiled<DT, BM, BN, WM, WN, NBUF, BL>, grid, block, args,
                            0, stream);
 }

@@ -143,3 +143,55 @@ def test_config_parity(hip_lib, forced, dtype):
     gemm(ea.to(dev), stored(eb).to(dev), P, kps, S)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(P.cpu().numpy().astype(np.float64), EP)
+
+
+# Large-tile configurations on grids of more workgroups than the chip has CUs
+# (6 x 6 tiles x 8 splits = 288): the first round starts staggered, later
+# rounds reuse the freed CUs.  The last column tile is 40 columns wide, every
+# full 16-bit split ends in a half chunk and the last split is short.  With
+# exact-arithmetic inputs every partial and the final sum are exact, so both
+# must match bit for bit (C is the binary64 sum of the exact partials).
+MULTI_ROUND = ([("nk", c, "bf16") for c in TILED] + [("kn", c, "bf16") for c in KN_TILED] +
+               [("nk", TILED[0], "f16"), ("nk", TILED[0], "f32")])
+
+
+@pytest.mark.gpu
+@pytest.mark.skipif(not gpu_available(), reason="no GPU")
+@pytest.mark.parametrize("case", MULTI_ROUND,
+                         ids=lambda c: f"{c[0]}:tiled," + ",".join(map(str, c[1])) + f"-{c[2]}")
+def test_tiled_multi_round_exact(hip_lib, case):
+    layout, cfg, dtype = case
+    bm, bn = cfg[0], cfg[1]
+    M, N, S, kps = 6 * bm, 5 * bn + 40, 8, 96
+    K = (S - 1) * kps + 64
+    old = os.environ.get("SPLITK_PLAN")
+    os.environ["SPLITK_PLAN"] = _plan_text("tiled", cfg)
+    try:
+        describe = hip_lib.describe if layout == "nk" else hip_lib.describe_bn
+        text = describe(M, N, K, kps, S, inputs.DTYPES[dtype])
+        print(f"case {layout} {dtype} M{M} N{N} K{K} kps{kps} S{S}: {text}", flush=True)
+        assert f"bm{bm} bn{bn}" in text and "grid288" in text, text
+        stored = (lambda t: t) if layout == "nk" else (lambda t: t.T.contiguous())
+        gemm_reduce = hip_lib.gemm_bt_reduce if layout == "nk" else hip_lib.gemm_bn_reduce
+        dev = torch.device("cuda:0")
+        ea, eb = inputs.exact_operands(M, N, K, dtype, seed=bm + bn + S)
+        ea64 = oracle.decode(inputs.stored_bits(ea), dtype)
+        eb64 = oracle.decode(inputs.stored_bits(eb), dtype)
+        EP, _, _ = oracle.splitk_partials(ea64, eb64, kps, S)
+        EC = EP.sum(axis=0)
+        pbuf = inputs.guarded_buffer(S * M * N, "nan").to(dev)
+        cbuf = inputs.guarded_buffer(M * N, "nan").to(dev)
+        gemm_reduce(ea.to(dev), stored(eb).to(dev), pbuf[: S * M * N].view(S, M, N),
+                    cbuf[: M * N].view(M, N), kps, S)
+        torch.cuda.synchronize()
+        p, c = pbuf.cpu().numpy(), cbuf.cpu().numpy()
+    finally:
+        if old is None:
+            os.environ.pop("SPLITK_PLAN", None)
+        else:
+            os.environ["SPLITK_PLAN"] = old
+    guard = np.float32(inputs.GUARD_VALUE).view(np.uint32)
+    assert np.all(p[S * M * N:].view(np.uint32) == guard)
+    assert np.all(c[M * N:].view(np.uint32) == guard)
+    np.testing.assert_array_equal(p[: S * M * N].astype(np.float64), EP.reshape(-1))
+    np.testing.assert_array_equal(c[: M * N].astype(np.float64), EC.reshape(-1))

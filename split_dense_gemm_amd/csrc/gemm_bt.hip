@@ -49,6 +49,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <type_traits>
 
 #include "splitk_internal.h"
 
@@ -123,6 +124,16 @@ __device__ __attribute__((always_inline)) inline TileId skinny_tile(int b, int n
     }
     const int rest = logical / tiles_m;
     return TileId{logical % tiles_m, rest % tiles_n, rest / tiles_n};
+}
+
+// Calls f(integral_constant<int, I>) for I = B .. E-1: a loop whose index
+// is a constant expression in the body.
+template <int B, int E, class F>
+__device__ __attribute__((always_inline)) inline void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
 }
 
 // LDS slot of 16-byte piece p of staged row r.  XOR-swizzled so that the
@@ -539,16 +550,23 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bt_tiled(const uint8_t* __r
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x16{};
 
-    // MFMA work of chunk c.  When `next` >= 0, the DMA of chunk `next` is
-    // issued a quarter after each of the four k-steps: issued all at once,
-    // the wave stalled ~1200 cycles per chunk waiting for the texture path to
-    // accept it, with no MFMA in flight (measured on 256x256 tiles; spread,
-    // the chunk's work went from ~4100 to ~3550 cycles).
+    // MFMA work of chunk c.  When `next` >= 0 the DMA of chunk `next` is
+    // issued between this chunk's MFMAs.  Issued all at once, the wave
+    // stalled ~1200 cycles per chunk waiting for the texture path to accept
+    // it, with no MFMA in flight (256x256 tiles: spread, the chunk's work
+    // went from ~4100 to ~3550 cycles).
+    //  * Two-buffer ring (256x256 tiles): the next chunk is the only one in
+    //    flight, so it is issued over the first two of the four k-steps, one
+    //    instruction per MFMA pair, pinned with scheduling barriers (the
+    //    scheduler otherwise bunches them).  Issued over all four k-steps,
+    //    its last quarter had no time to land before it was needed.
+    //  * Deeper rings: a quarter after each k-step, as the scheduler places it.
+    constexpr int DMA_STEPS = NBUF == 2 ? 2 : 4;
     auto compute = [&](int c, int next) {
         const uint8_t* lds = smem + (c % NBUF) * BUF;
         const int steps = half_chunk(c) ? 2 : 4;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        static_for<0, 4>([&](auto qv) {
+            constexpr int q = decltype(qv)::value;
             u32x4 fa[MB], fb[NB];
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) {
@@ -572,8 +590,22 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bt_tiled(const uint8_t* __r
 #pragma unroll
                     for (int nb = 0; nb < NB; ++nb)
                         acc[mb][nb] = Op::step(fa[mb], fb[nb], acc[mb][nb], e);
-            if (next >= 0) dma(next, q * DPW / 4, (q + 1) * DPW / 4);
-        }
+            if constexpr (q < DMA_STEPS) {
+                constexpr int LO = q * DPW / DMA_STEPS, ND = (q + 1) * DPW / DMA_STEPS - LO;
+                if (next >= 0) {
+                    dma(next, LO, LO + ND);
+                    if constexpr (NBUF == 2) {
+                        constexpr int NM = Op::kStepsPerPiece * MB * NB;
+                        static_for<0, ND>([&](auto jv) {
+                            constexpr int j = decltype(jv)::value;
+                            constexpr int G = (j + 1) * NM / ND - j * NM / ND;  // MFMAs before DMA j
+                            if constexpr (G > 0) __builtin_amdgcn_sched_group_barrier(0x008, G, 0);
+                            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one VMEM load
+                        });
+                    }
+                }
+            }
+        });
     };
 
     // Prologue: the first NBUF - 1 chunks in flight.

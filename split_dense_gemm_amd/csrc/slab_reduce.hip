@@ -30,21 +30,30 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBlock = 256;
 
-// Store of one 16-byte F32 word as output type OT (0 F32, 1 F16, 2 BF16).
-template <int OT>
+// Store of one 16-byte F32 word as output type OT (0 F32, 1 F16, 2 BF16),
+// as a streaming (nontemporal) store when NT.
+template <int OT, bool NT = false>
 __device__ inline void store4(void* C, int64_t g, f32x4 v) {
-    if (OT == 0) {
-        ((f32x4*)C)[g] = v;
-    } else if (OT == 1) {
-        ((f16x4*)C)[g] = __builtin_convertvector(v, f16x4);
+    if constexpr (OT == 0) {
+        if constexpr (NT) __builtin_nontemporal_store(v, &((f32x4*)C)[g]);
+        else ((f32x4*)C)[g] = v;
+    } else if constexpr (OT == 1) {
+        const f16x4 h = __builtin_convertvector(v, f16x4);
+        if constexpr (NT) __builtin_nontemporal_store(h, &((f16x4*)C)[g]);
+        else ((f16x4*)C)[g] = h;
     } else {
-        ((bf16x4*)C)[g] = __builtin_convertvector(v, bf16x4);
+        const bf16x4 h = __builtin_convertvector(v, bf16x4);
+        if constexpr (NT) __builtin_nontemporal_store(h, &((bf16x4*)C)[g]);
+        else ((bf16x4*)C)[g] = h;
     }
 }
 
 // Slab word load of the flat pass: streaming (nontemporal) when the slabs
 // are too large for the memory-side cache (NT, see stream_slabs), normal
-// otherwise.  Each word is read once.
+// otherwise.  Each word is read once.  With NT the sums are stored as
+// streaming writes too: 8 slabs of 2048x4096 took 53.8 us with normal C
+// stores and 50.7 us with streaming ones (a read-only pass over the same
+// slabs takes 43.7 us).
 template <bool NT>
 __device__ inline f32x4 load_slab(const f32x4* p) {
     if constexpr (NT) return __builtin_nontemporal_load(p);
@@ -74,7 +83,7 @@ __global__ __launch_bounds__(kBlock) void slab_reduce_kernel(const f32x4* __rest
                 f32x4 acc = v[it][0];
 #pragma unroll
                 for (int s = 1; s < S; ++s) acc += v[it][s];
-                store4<OT>(C, g, acc);
+                store4<OT, NT>(C, g, acc);
             }
         }
     } else {
@@ -94,7 +103,7 @@ __global__ __launch_bounds__(kBlock) void slab_reduce_kernel(const f32x4* __rest
                 for (int j = 0; j < kBatch; ++j) acc += v[j];
             }
             for (; s < splits; ++s) acc += load_slab<NT>(&P[(int64_t)s * plane4 + g]);
-            store4<OT>(C, g, acc);
+            store4<OT, NT>(C, g, acc);
         }
     }
 }

@@ -409,3 +409,20 @@ def test_typed_reduce_alone_bitwise(sdg, out, S, M, N):
     ref, _, _ = oracle.slab_sum(slabs.numpy())   # exact: multiples of 1/64 well inside F32
     np.testing.assert_array_equal(bits[: M * N], oracle.encode(ref, out).ravel())
     assert np.all(bits[M * N:] == GUARD16[out])
+
+
+@pytest.mark.parametrize("out", ["f16", "bf16"])
+@pytest.mark.parametrize("S,M,N", [(13, 2048, 2048), (4, 4096, 4096)])
+def test_typed_reduce_streaming_bitwise(sdg, out, S, M, N):
+    """More than 192 MiB of slabs: streaming loads and streaming 8-byte
+    stores of the rounded sums (one case in batches of eight slabs)."""
+    dev = torch.device("cuda:0")
+    gen = torch.Generator().manual_seed(S + M + 7)
+    slabs = torch.randint(-4000, 4000, (S, M, N), generator=gen).float().div_(64)
+    cbuf = inputs.guarded_buffer(M * N, "nan", dtype=out).to(dev)
+    sdg.reduce(slabs.to(dev), cbuf[: M * N].view(M, N), S)
+    torch.cuda.synchronize()
+    bits = inputs.stored_bits(cbuf.cpu())
+    ref, _, _ = oracle.slab_sum(slabs.numpy())
+    np.testing.assert_array_equal(bits[: M * N], oracle.encode(ref, out).ravel())
+    assert np.all(bits[M * N:] == GUARD16[out])

@@ -562,9 +562,11 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bt_tiled(const uint8_t* __r
     //    its last quarter had no time to land before it was needed.
     //  * Deeper rings: a quarter after each k-step, as the scheduler places it.
     constexpr int DMA_STEPS = NBUF == 2 ? 2 : 4;
-    auto compute = [&](int c, int next) {
+    // `may_be_half` is false for the steady-state chunks: only a split's last
+    // chunk can be half empty, and it always falls in the tail loop.
+    auto compute = [&](int c, int next, auto may_be_half) {
         const uint8_t* lds = smem + (c % NBUF) * BUF;
-        const int steps = half_chunk(c) ? 2 : 4;
+        const int steps = (decltype(may_be_half)::value && half_chunk(c)) ? 2 : 4;
         static_for<0, 4>([&](auto qv) {
             constexpr int q = decltype(qv)::value;
             u32x4 fa[MB], fb[NB];
@@ -572,7 +574,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bt_tiled(const uint8_t* __r
             for (int mb = 0; mb < MB; ++mb) {
                 const int row = wm * TM + mb * 32 + r;
                 fa[mb] = *(const u32x4*)(lds + row * kChunkBytes + slot_of(row, 2 * q + h) * 16);
-                if (q >= 2) fa[mb] = q < steps ? fa[mb] : u32x4{};
+                if (decltype(may_be_half)::value && q >= 2) fa[mb] = q < steps ? fa[mb] : u32x4{};
             }
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
@@ -628,13 +630,13 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bt_tiled(const uint8_t* __r
     for (; c + NBUF - 1 < nchunks; ++c) {
         __builtin_amdgcn_s_waitcnt(SPLITK_VMCNT((NBUF - 2) * DPW));
         lds_barrier();  // chunk c complete for all waves; slot of chunk c-1 free
-        compute(c, c + NBUF - 1);
+        compute(c, c + NBUF - 1, std::false_type{});
     }
     // Tail: no more loads to issue; wait for everything still in flight.
     for (; c < nchunks; ++c) {
         __builtin_amdgcn_s_waitcnt(SPLITK_VMCNT(0));
         lds_barrier();
-        compute(c, -1);
+        compute(c, -1, std::true_type{});
     }
 
     // Register i of lane l holds row 8*(i/4) + 4*(l/32) + i%4, column l%32.

@@ -489,7 +489,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bt_tiled(const uint8_t* __r
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    // Uniform in a wave; as a scalar it gives the DMA instructions' LDS
+    // addresses without a lane read per instruction.
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WN, wn = wave % WN;
     const int r = lane & 31;
     const int h = lane >> 5;
@@ -519,11 +521,27 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bt_tiled(const uint8_t* __r
                      (size_t)k0 * ES;
         }
     }
+    // Chunk 0 address of each DMA instruction for a full chunk, the piece
+    // folded in: a full chunk c adds one uniform offset.
+    const uint8_t* full[DPW];
+#pragma unroll
+    for (int i = 0; i < DPW; ++i) full[i] = src[i] + piece[i] * 16;
     // DMA instructions [lo, hi) of chunk c, into ring slot c % NBUF.  In a
     // half chunk the lanes meant for pieces 4..7 re-read pieces 0..3 (in
     // bounds); those copies are finite and meet zero A fragments in compute().
-    auto dma = [&](int c, int lo, int hi) {
+    // `may_be_half` false: the caller knows chunk c is full.
+    auto dma = [&](int c, int lo, int hi, auto may_be_half) {
         uint8_t* buf = smem + (c % NBUF) * BUF;
+        if constexpr (!decltype(may_be_half)::value) {
+            const size_t off = (size_t)c * kChunkBytes;
+            const size_t off_kn = (size_t)c * CK * row_bytes_b;
+#pragma unroll
+            for (int i = lo; i < hi; ++i)
+                __builtin_amdgcn_global_load_lds(
+                    (const void*)(full[i] + (BL == 1 && i >= IA ? off_kn : off)),
+                    (__attribute__((address_space(3))) void*)(buf + (i * NW + wave) * 1024), 16, 0, 0);
+            return;
+        }
         const bool half = half_chunk(c);
         const int mask = half ? 3 : 7;
         const size_t off = (size_t)c * kChunkBytes;
@@ -564,7 +582,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bt_tiled(const uint8_t* __r
     constexpr int DMA_STEPS = NBUF == 2 ? 2 : 4;
     // `may_be_half` is false for the steady-state chunks: only a split's last
     // chunk can be half empty, and it always falls in the tail loop.
-    auto compute = [&](int c, int next, auto may_be_half) {
+    auto compute = [&](int c, int next, auto may_be_half, auto next_may_be_half) {
         const uint8_t* lds = smem + (c % NBUF) * BUF;
         const int steps = (decltype(may_be_half)::value && half_chunk(c)) ? 2 : 4;
         static_for<0, 4>([&](auto qv) {
@@ -595,7 +613,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bt_tiled(const uint8_t* __r
             if constexpr (q < DMA_STEPS) {
                 constexpr int LO = q * DPW / DMA_STEPS, ND = (q + 1) * DPW / DMA_STEPS - LO;
                 if (next >= 0) {
-                    dma(next, LO, LO + ND);
+                    dma(next, LO, LO + ND, next_may_be_half);
                     if constexpr (NBUF == 2) {
                         constexpr int NM = Op::kStepsPerPiece * MB * NB;
                         static_for<0, ND>([&](auto jv) {
@@ -613,7 +631,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bt_tiled(const uint8_t* __r
     // Prologue: the first NBUF - 1 chunks in flight.
 #pragma unroll
     for (int j = 0; j < NBUF - 1; ++j)
-        if (j < nchunks) dma(j, 0, DPW);
+        if (j < nchunks) dma(j, 0, DPW, std::true_type{});
     // Staggered start.  On a grid of several rounds the CUs would otherwise
     // run in lockstep: all of them store their partial tiles at the same
     // moment, each at 1/256 of the write bandwidth while no MFMA work runs
@@ -625,18 +643,26 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bt_tiled(const uint8_t* __r
         for (int i = 0; i < slot; ++i) __builtin_amdgcn_s_sleep(8);
     }
     // Steady state: every pass issues one more chunk, so exactly NBUF - 2
-    // younger chunks (DPW loads each) are outstanding behind chunk c.
+    // younger chunks (DPW loads each) are outstanding behind chunk c.  Only
+    // a split's last chunk can be half empty: the passes before the one
+    // that issues it know that both their chunk and the issued one are full.
     int c = 0;
-    for (; c + NBUF - 1 < nchunks; ++c) {
+    for (; c + NBUF < nchunks; ++c) {
         __builtin_amdgcn_s_waitcnt(SPLITK_VMCNT((NBUF - 2) * DPW));
         lds_barrier();  // chunk c complete for all waves; slot of chunk c-1 free
-        compute(c, c + NBUF - 1, std::false_type{});
+        compute(c, c + NBUF - 1, std::false_type{}, std::false_type{});
+    }
+    if (c + NBUF - 1 < nchunks) {  // issues the last chunk
+        __builtin_amdgcn_s_waitcnt(SPLITK_VMCNT((NBUF - 2) * DPW));
+        lds_barrier();
+        compute(c, c + NBUF - 1, std::false_type{}, std::true_type{});
+        ++c;
     }
     // Tail: no more loads to issue; wait for everything still in flight.
     for (; c < nchunks; ++c) {
         __builtin_amdgcn_s_waitcnt(SPLITK_VMCNT(0));
         lds_barrier();
-        compute(c, -1, std::true_type{});
+        compute(c, -1, std::true_type{}, std::true_type{});
     }
 
     // Register i of lane l holds row 8*(i/4) + 4*(l/32) + i%4, column l%32.

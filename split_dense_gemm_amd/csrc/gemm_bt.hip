@@ -526,35 +526,28 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bt_tiled(const uint8_t* __r
     const uint8_t* full[DPW];
 #pragma unroll
     for (int i = 0; i < DPW; ++i) full[i] = src[i] + piece[i] * 16;
-    // DMA instructions [lo, hi) of chunk c, into ring slot c % NBUF.  In a
-    // half chunk the lanes meant for pieces 4..7 re-read pieces 0..3 (in
-    // bounds); those copies are finite and meet zero A fragments in compute().
+    // In a half chunk the lanes meant for pieces 4..7 re-read pieces 0..3
+    // (in bounds); those copies are finite and meet zero A fragments in
+    // compute().  That is piece & 3 instead of piece, i.e. (piece & 4) * 16
+    // bytes lower.  Bit 2 of a lane's piece is the same in every instruction:
+    // slot_of(8g + lane/8, lane%8) differs between row groups g only in bit 0.
+    const int half_back = (slot_of(lane >> 3, lane & 7) & 4) * 16;
+    // DMA instructions [lo, hi) of chunk c, into ring slot c % NBUF.
     // `may_be_half` false: the caller knows chunk c is full.
     auto dma = [&](int c, int lo, int hi, auto may_be_half) {
         uint8_t* buf = smem + (c % NBUF) * BUF;
-        if constexpr (!decltype(may_be_half)::value) {
-            const size_t off = (size_t)c * kChunkBytes;
-            const size_t off_kn = (size_t)c * CK * row_bytes_b;
-#pragma unroll
-            for (int i = lo; i < hi; ++i)
-                __builtin_amdgcn_global_load_lds(
-                    (const void*)(full[i] + (BL == 1 && i >= IA ? off_kn : off)),
-                    (__attribute__((address_space(3))) void*)(buf + (i * NW + wave) * 1024), 16, 0, 0);
-            return;
-        }
-        const bool half = half_chunk(c);
-        const int mask = half ? 3 : 7;
+        const bool half = decltype(may_be_half)::value && half_chunk(c);
         const size_t off = (size_t)c * kChunkBytes;
+        const size_t off_kn = (size_t)c * CK * row_bytes_b;
 #pragma unroll
         for (int i = lo; i < hi; ++i) {
             const uint8_t* g;
             if (BL == 1 && i >= IA) {
                 // B as [K,N]: in a half chunk the second half of the k-rows
                 // re-reads the first half (in bounds, never consumed).
-                const size_t up = (half && i >= IH) ? (size_t)(CK / 2) * row_bytes_b : 0;
-                g = src[i] + (size_t)c * CK * row_bytes_b - up;
+                g = full[i] + off_kn - ((half && i >= IH) ? (size_t)(CK / 2) * row_bytes_b : 0);
             } else {
-                g = src[i] + off + (piece[i] & mask) * 16;
+                g = full[i] + off - (half ? half_back : 0);
             }
             __builtin_amdgcn_global_load_lds((const void*)g,
                                              (__attribute__((address_space(3))) void*)(buf + (i * NW + wave) * 1024),
@@ -585,46 +578,66 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bt_tiled(const uint8_t* __r
     auto compute = [&](int c, int next, auto may_be_half, auto next_may_be_half) {
         const uint8_t* lds = smem + (c % NBUF) * BUF;
         const int steps = (decltype(may_be_half)::value && half_chunk(c)) ? 2 : 4;
-        static_for<0, 4>([&](auto qv) {
+        // Fragments of k-step q into fa[q % 2], fb[q % 2].  With the
+        // two-buffer ring (PIPE) step q + 1's are read while step q's MFMAs
+        // run, pinned by scheduling groups: 1-2% on 256x256 tiles.  The
+        // deeper rings keep the compiler's order, reads just before their
+        // step (the pinned order was 6% slower on 256x128 with 2x4 waves).
+        constexpr bool PIPE = NBUF == 2;
+        u32x4 fa[2][MB], fb[2][NB];
+        auto frags = [&](auto qv) {
             constexpr int q = decltype(qv)::value;
-            u32x4 fa[MB], fb[NB];
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) {
                 const int row = wm * TM + mb * 32 + r;
-                fa[mb] = *(const u32x4*)(lds + row * kChunkBytes + slot_of(row, 2 * q + h) * 16);
-                if (decltype(may_be_half)::value && q >= 2) fa[mb] = q < steps ? fa[mb] : u32x4{};
+                u32x4 v = *(const u32x4*)(lds + row * kChunkBytes + slot_of(row, 2 * q + h) * 16);
+                if (decltype(may_be_half)::value && q >= 2) v = q < steps ? v : u32x4{};
+                fa[q & 1][mb] = v;
             }
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
                 if (BL == 1) {
-                    fb[nb] = kn_frag<DT, BN>(lds + BM * kChunkBytes, q, wn * (TN / 32) + nb, lane);
+                    fb[q & 1][nb] = kn_frag<DT, BN>(lds + BM * kChunkBytes, q, wn * (TN / 32) + nb, lane);
                 } else {
                     const int row = BM + wn * TN + nb * 32 + r;
-                    fb[nb] = *(const u32x4*)(lds + row * kChunkBytes + slot_of(row, 2 * q + h) * 16);
+                    fb[q & 1][nb] = *(const u32x4*)(lds + row * kChunkBytes + slot_of(row, 2 * q + h) * 16);
                 }
             }
+        };
+        constexpr int NREAD = MB + NB * (BL == 1 ? (DT == 0 ? 4 : 2) : 1);  // LDS reads per step
+        constexpr int NM = Op::kStepsPerPiece * MB * NB;                     // MFMAs per step
+        frags(std::integral_constant<int, 0>{});
+        if constexpr (PIPE) __builtin_amdgcn_sched_group_barrier(0x100, NREAD, 0);  // step 0's reads first
+        static_for<0, 4>([&](auto qv) {
+            constexpr int q = decltype(qv)::value;
+            if constexpr (PIPE && q < 3) frags(std::integral_constant<int, q + 1>{});
+            if constexpr (!PIPE && q > 0) frags(qv);
 #pragma unroll
             for (int e = 0; e < Op::kStepsPerPiece; ++e)
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
                     for (int nb = 0; nb < NB; ++nb)
-                        acc[mb][nb] = Op::step(fa[mb], fb[nb], acc[mb][nb], e);
+                        acc[mb][nb] = Op::step(fa[q & 1][mb], fb[q & 1][nb], acc[mb][nb], e);
+            // Schedule: the next step's LDS reads ahead of this step's MFMAs.
+            if constexpr (PIPE && q < 3) __builtin_amdgcn_sched_group_barrier(0x100, NREAD, 0);
+            bool pinned = !PIPE;
             if constexpr (q < DMA_STEPS) {
                 constexpr int LO = q * DPW / DMA_STEPS, ND = (q + 1) * DPW / DMA_STEPS - LO;
                 if (next >= 0) {
                     dma(next, LO, LO + ND, next_may_be_half);
                     if constexpr (NBUF == 2) {
-                        constexpr int NM = Op::kStepsPerPiece * MB * NB;
                         static_for<0, ND>([&](auto jv) {
                             constexpr int j = decltype(jv)::value;
                             constexpr int G = (j + 1) * NM / ND - j * NM / ND;  // MFMAs before DMA j
                             if constexpr (G > 0) __builtin_amdgcn_sched_group_barrier(0x008, G, 0);
                             __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one VMEM load
                         });
+                        pinned = true;
                     }
                 }
             }
+            if (!pinned) __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
         });
     };
 

@@ -114,16 +114,16 @@ struct Mfma<0> {  // F32: four 32x32x2 MFMAs per 4-element piece, one element ea
 struct TileId {
     int mt, nt, s;  // row tile, column tile, split
 };
-__device__ __attribute__((always_inline)) inline TileId skinny_tile(int b, int n, int tiles_m,
-                                                                    int tiles_n, int order) {
-    const int logical = xcd_logical_id(b, n);
-    if (order == 1) {
-        const int splits = n / (tiles_m * tiles_n);
-        const int u = logical / splits;
-        return TileId{u % tiles_m, u / tiles_m, logical % splits};
+__device__ __attribute__((always_inline)) inline TileId skinny_tile(int b, int n, const TileGrid& g) {
+    const uint32_t logical = (uint32_t)xcd_logical_id(b, n);
+    if (g.order == 1) {
+        const uint32_t u = fastdiv(logical, g.by_splits);
+        const uint32_t nt = fastdiv(u, g.by_tiles_m);
+        return TileId{(int)(u - nt * g.tiles_m), (int)nt, (int)(logical - u * g.splits)};
     }
-    const int rest = logical / tiles_m;
-    return TileId{logical % tiles_m, rest % tiles_n, rest / tiles_n};
+    const uint32_t rest = fastdiv(logical, g.by_tiles_m);
+    const uint32_t s = fastdiv(rest, g.by_tiles_n);
+    return TileId{(int)(logical - rest * g.tiles_m), (int)(rest - s * g.tiles_n), (int)s};
 }
 
 // Calls f(integral_constant<int, I>) for I = B .. E-1: a loop whose index
@@ -273,7 +273,7 @@ template <int DT, int BM, int BN, int W, int D, int BL>
 __global__ __launch_bounds__(W * 64) void gemm_bt_wavek(const uint8_t* __restrict__ A,
                                                         const uint8_t* __restrict__ B,
                                                         float* __restrict__ P, int M, int N, int K,
-                                                        int kps, int tiles_m, int tiles_n, int order) {
+                                                        int kps, TileGrid tg) {
     using Op = Mfma<DT>;
     constexpr int ES = Op::kElemBytes;
     constexpr int CK = kChunkBytes / ES;  // elements per chunk
@@ -291,7 +291,7 @@ __global__ __launch_bounds__(W * 64) void gemm_bt_wavek(const uint8_t* __restric
     constexpr int RED_BYTES = W * BN * (BM + 4) * 4;  // sum_and_store's tiles
     __shared__ __attribute__((aligned(16))) uint8_t smem[STAGE_BYTES > RED_BYTES ? STAGE_BYTES : RED_BYTES];
 
-    const TileId tile = skinny_tile(blockIdx.x, gridDim.x, tiles_m, tiles_n, order);
+    const TileId tile = skinny_tile(blockIdx.x, gridDim.x, tg);
     const int mt = tile.mt, nt = tile.nt, s = tile.s;
 
     const int lane = threadIdx.x & 63;
@@ -311,6 +311,16 @@ __global__ __launch_bounds__(W * 64) void gemm_bt_wavek(const uint8_t* __restric
     const size_t row_bytes = (size_t)K * ES;
     const size_t row_bytes_b = (size_t)N * ES;  // [K,N] layout: one k-row of B
     const int lrow = lane >> 3, lslot = lane & 7;
+    // Row 8*i + lrow of the A (then B) rows: one base per operand and a
+    // uniform stride of 8 rows, so that the loads go out without a 64-bit
+    // multiply each.  B rows past N (a tail tile) re-read row N-1 (row
+    // offsets grow with the row, so clamping the offset clamps the row);
+    // those columns are never stored.  Every address stays B or A plus an
+    // offset, so the compiler keeps global (not flat) loads.
+    const size_t stride8 = (size_t)8 * row_bytes;
+    const uint8_t* a0 = A + ((size_t)mt * BM + lrow) * row_bytes + (size_t)k0 * ES;
+    const size_t b0 = ((size_t)nt * BN + lrow) * row_bytes + (size_t)k0 * ES;  // offsets from B
+    const size_t b_last = (size_t)(N - 1) * row_bytes + (size_t)k0 * ES;
     const uint8_t* src[LOADS];
     int piece[LOADS];
 #pragma unroll
@@ -322,11 +332,11 @@ __global__ __launch_bounds__(W * 64) void gemm_bt_wavek(const uint8_t* __restric
             src[i] = B + (size_t)k0 * row_bytes_b +
                      kn_src<ES, BN>(row - BM, lslot, row_bytes_b, (size_t)nt * BN * ES);
             piece[i] = 0;
+        } else if (i < BM / 8) {
+            src[i] = a0 + (size_t)i * stride8;
         } else {
-            // B rows past N (a tail tile) re-read row N-1; never stored.
-            src[i] = row < BM ? A + (size_t)(mt * BM + row) * row_bytes
-                              : B + (size_t)min(nt * BN + row - BM, N - 1) * row_bytes;
-            src[i] += (size_t)k0 * ES;
+            const size_t o = b0 + (size_t)(i - BM / 8) * stride8;
+            src[i] = B + (o < b_last ? o : b_last);
         }
     }
     uint8_t* lds = smem + wave * ROWS * kChunkBytes;
@@ -779,8 +789,7 @@ template <int DT, int BM, int BN, int W, int R>
 __global__ __launch_bounds__(W * 64) void gemm_bt_wavek_dma(const uint8_t* __restrict__ A,
                                                             const uint8_t* __restrict__ B,
                                                             float* __restrict__ P, int M, int N,
-                                                            int K, int kps, int tiles_m,
-                                                            int tiles_n, int order) {
+                                                            int K, int kps, TileGrid tg) {
     using Op = Mfma<DT>;
     constexpr int ES = Op::kElemBytes;
     constexpr int CK = kChunkBytes / ES;
@@ -797,7 +806,7 @@ __global__ __launch_bounds__(W * 64) void gemm_bt_wavek_dma(const uint8_t* __res
     __shared__ __attribute__((aligned(16))) uint8_t tr_lds[W][BLOCK];
     __shared__ __attribute__((aligned(16))) uint8_t dma_lds[W][ROWS * kChunkBytes];
 
-    const TileId tile = skinny_tile(blockIdx.x, gridDim.x, tiles_m, tiles_n, order);
+    const TileId tile = skinny_tile(blockIdx.x, gridDim.x, tg);
     const int mt = tile.mt, nt = tile.nt, s = tile.s;
 
     const int lane = threadIdx.x & 63;
@@ -816,15 +825,23 @@ __global__ __launch_bounds__(W * 64) void gemm_bt_wavek_dma(const uint8_t* __res
 
     const size_t row_bytes = (size_t)K * ES;
     const int lrow = lane >> 3;
+    // As in gemm_bt_wavek: per-operand bases, a uniform 8-row stride, B rows
+    // past N clamped to row N-1 by their offset.
+    const size_t stride8 = (size_t)8 * row_bytes;
+    const uint8_t* a0 = A + ((size_t)mt * BM + lrow) * row_bytes + (size_t)k0 * ES;
+    const size_t b0 = ((size_t)nt * BN + lrow) * row_bytes + (size_t)k0 * ES;  // offsets from B
+    const size_t b_last = (size_t)(N - 1) * row_bytes + (size_t)k0 * ES;
     const uint8_t* src[LOADS];
     int piece[LOADS];
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
-        const int row = 8 * i + lrow;
-        src[i] = (row < BM ? A + (size_t)(mt * BM + row) * row_bytes
-                           : B + (size_t)min(nt * BN + row - BM, N - 1) * row_bytes) +
-                 (size_t)k0 * ES;
-        piece[i] = slot_of(row, lane & 7);
+        if (i < BM / 8) {
+            src[i] = a0 + (size_t)i * stride8;
+        } else {
+            const size_t o = b0 + (size_t)(i - BM / 8) * stride8;
+            src[i] = B + (o < b_last ? o : b_last);
+        }
+        piece[i] = slot_of(8 * i + lrow, lane & 7);
     }
     uint8_t* tr = &tr_lds[wave][0];            // 4 KiB transpose block
     uint8_t* dma_area = &dma_lds[wave][0];     // one whole chunk
@@ -927,7 +944,8 @@ hipError_t launch_wavek_dma(const void* A, const void* B, float* P, int64_t M, i
     const uint8_t* a = (const uint8_t*)A;
     const uint8_t* b = (const uint8_t*)B;
     int m = (int)M, n = (int)N, k = (int)K, kp = (int)kps;
-    void* args[] = {&a, &b, &P, &m, &n, &k, &kp, (void*)&tiles_m, (void*)&tiles_n, &order};
+    TileGrid tg = make_tile_grid(tiles_m, tiles_n, (int)splits, order);
+    void* args[] = {&a, &b, &P, &m, &n, &k, &kp, &tg};
     return hipLaunchKernel((const void*)&gemm_bt_wavek_dma<DT, BM, BN, W, R>, grid, dim3(W * 64), args,
                            0, stream);
 }
@@ -941,7 +959,8 @@ hipError_t launch_wavek(const void* A, const void* B, float* P, int64_t M, int64
     const uint8_t* a = (const uint8_t*)A;
     const uint8_t* b = (const uint8_t*)B;
     int m = (int)M, n = (int)N, k = (int)K, kp = (int)kps;
-    void* args[] = {&a, &b, &P, &m, &n, &k, &kp, (void*)&tiles_m, (void*)&tiles_n, &order};
+    TileGrid tg = make_tile_grid(tiles_m, tiles_n, (int)splits, order);
+    void* args[] = {&a, &b, &P, &m, &n, &k, &kp, &tg};
     return hipLaunchKernel((const void*)&gemm_bt_wavek<DT, BM, BN, W, D, BL>, grid, block, args, 0,
                            stream);
 }

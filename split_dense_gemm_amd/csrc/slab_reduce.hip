@@ -162,14 +162,14 @@ constexpr int tile_bands(int bm, int bn) { return bm * bn / (4 * kBlock) > 1 ? b
 template <int S, int BM, int BN, int OT>
 __global__ __launch_bounds__(kBlock) void slab_reduce_tiles(const float* __restrict__ P,
                                                             void* __restrict__ C, int M, int N,
-                                                            int tiles_m) {
+                                                            int tiles_m, FastDiv by_tiles_m) {
     constexpr int C4 = BN / 4;                  // 16-byte words per tile row
     constexpr int PT = tile_bands(BM, BN);      // workgroups per tile
     constexpr int ITEMS = BM * C4 / PT / kBlock;  // words per lane
     static_assert(ITEMS >= 1 && BM * C4 % (PT * kBlock) == 0, "tile size");
     const int lr = xcd_logical_id(blockIdx.x, gridDim.x);
     const int u = lr / PT, band = lr % PT;
-    const int mt = u % tiles_m, nt = u / tiles_m;
+    const int nt = (int)fastdiv((uint32_t)u, by_tiles_m), mt = u - nt * tiles_m;
     const int valid4 = min(C4, (N - nt * BN) / 4);  // words of a tile row inside N
     const int64_t plane = (int64_t)M * N;
     const float* tile = P + ((int64_t)mt * BM + band * (BM / PT)) * N + (int64_t)nt * BN;
@@ -200,7 +200,8 @@ template <int S, int BM, int BN, int OT>
 hipError_t launch_tiles(const float* partials, void* C, int64_t M, int64_t N, hipStream_t stream) {
     const int tiles_m = (int)(M / BM), tiles_n = (int)((N + BN - 1) / BN);
     int m = (int)M, n = (int)N, tm = tiles_m;
-    void* args[] = {(void*)&partials, &C, &m, &n, &tm};
+    FastDiv by_tm = make_fastdiv((uint32_t)tiles_m);
+    void* args[] = {(void*)&partials, &C, &m, &n, &tm, &by_tm};
     return hipLaunchKernel((const void*)&slab_reduce_tiles<S, BM, BN, OT>,
                            dim3((unsigned)(tiles_m * tiles_n * tile_bands(BM, BN))), dim3(kBlock), args, 0,
                            stream);

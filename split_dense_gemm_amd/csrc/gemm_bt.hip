@@ -216,15 +216,24 @@ __device__ inline void sum_and_store(float* lds, const f32x16 (&acc)[MB][NB], fl
                                  acc[mb][nb][4 * g + 3]};
                 *(f32x4*)(mine + (nb * 32 + r) * CP + mb * 32 + 8 * g + 4 * h) = v;
             }
+    // The slab pointer is needed only for the stores below; materialized
+    // here, its argument load is not left on the path after the barrier.
+    asm volatile("" ::"s"(out));
     __syncthreads();
     for (int it = threadIdx.x; it < BN * (BM / 4); it += W * 64) {
         const int col = it % BN, rq = it / BN;
-        f32x4 v = *(const f32x4*)(lds + col * CP + 4 * rq);
+        // All W reads first, then the adds in ascending wave order.
+        f32x4 t[W];
 #pragma unroll
-        for (int w = 1; w < W; ++w) v += *(const f32x4*)(lds + w * TS + col * CP + 4 * rq);
+        for (int w = 0; w < W; ++w) t[w] = *(const f32x4*)(lds + w * TS + col * CP + 4 * rq);
+        __builtin_amdgcn_sched_group_barrier(0x100, W, 0);  // the reads ahead of every add
+        f32x4 v = t[0];
+#pragma unroll
+        for (int w = 1; w < W; ++w) v += t[w];
         if (col < valid) {
+            float* o = out + (size_t)(4 * rq) * N + col;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) out[(size_t)(4 * rq + e) * N + col] = v[e];
+            for (int e = 0; e < 4; ++e) o[(size_t)e * N] = v[e];
         }
     }
 }

@@ -472,7 +472,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bt_tiled(const uint8_t* __r
                                                               float* __restrict__ P, int M, int N,
                                                               int K, int kps, int tiles_m,
                                                               int tiles_n, int streaming,
-                                                              int stagger) {
+                                                              int stagger, int order) {
     using Op = Mfma<DT>;
     constexpr int ES = Op::kElemBytes;
     constexpr int CK = kChunkBytes / ES;
@@ -492,19 +492,31 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bt_tiled(const uint8_t* __r
     static_assert((BM / 8) % NW == 0 && ((BM + BN / 2) / 8) % NW == 0, "row split per wave");
     __shared__ __attribute__((aligned(16))) uint8_t smem[NBUF * BUF];
 
-    // Tile order: split major; inside a split, groups of GM row tiles sweep
-    // all column tiles, so the workgroups resident on one XCD at a time share
-    // a few A and B panels in its L2.
+    // Tile order 0: split major; inside a split, groups of GM row tiles
+    // sweep all column tiles, so the workgroups resident on one XCD at a time
+    // share a few A and B panels in its L2.  Order 1: split fastest, then M,
+    // then N, so that every slab of a tile comes from one XCD (each XCD
+    // takes a contiguous range of logical ids) and the tile-ordered slab sum
+    // finds it in that XCD's L2.
     const int logical = xcd_logical_id(blockIdx.x, gridDim.x);
     const int per_split = tiles_m * tiles_n;
-    const int s = logical / per_split;
-    const int t = logical % per_split;
-    const int gm = min(GM, tiles_m);
-    const int group = t / (gm * tiles_n);
-    const int in_group = t % (gm * tiles_n);
-    const int rows_here = min(gm, tiles_m - group * gm);
-    const int mt = group * gm + in_group % rows_here;
-    const int nt = in_group / rows_here;
+    int s, mt, nt;
+    if (order == 1) {
+        const int splits = gridDim.x / per_split;
+        const int t = logical / splits;
+        s = logical - t * splits;
+        nt = t / tiles_m;
+        mt = t - nt * tiles_m;
+    } else {
+        s = logical / per_split;
+        const int t = logical % per_split;
+        const int gm = min(GM, tiles_m);
+        const int group = t / (gm * tiles_n);
+        const int in_group = t % (gm * tiles_n);
+        const int rows_here = min(gm, tiles_m - group * gm);
+        mt = group * gm + in_group % rows_here;
+        nt = in_group / rows_here;
+    }
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -754,7 +766,7 @@ int device_cus() {
 
 template <int DT, int BM, int BN, int WM, int WN, int NBUF, int BL>
 hipError_t launch_tiled(const void* A, const void* B, float* P, int64_t M, int64_t N, int64_t K,
-                        int64_t kps, int64_t splits, hipStream_t stream) {
+                        int64_t kps, int64_t splits, int order, hipStream_t stream) {
     const int tiles_m = (int)(M / BM), tiles_n = (int)((N + BN - 1) / BN);
     const dim3 grid((unsigned)(tiles_m * (int64_t)tiles_n * splits));
     const dim3 block(WM * WN * 64);
@@ -766,7 +778,8 @@ hipError_t launch_tiled(const void* A, const void* B, float* P, int64_t M, int64
     // the first device_cus() workgroups are the first round.
     const int cus = device_cus();
     int stagger = (int64_t)grid.x > cus ? cus : 0;
-    void* args[] = {&a, &b, &P, &m, &n, &k, &kp, (void*)&tiles_m, (void*)&tiles_n, &streaming, &stagger};
+    void* args[] = {&a, &b, &P, &m, &n, &k, &kp, (void*)&tiles_m, (void*)&tiles_n, &streaming, &stagger,
+                    &order};
     return hipLaunchKernel((const void*)&gemm_bt_tiled<DT, BM, BN, WM, WN, NBUF, BL>, grid, block, args,
                            0, stream);
 }
@@ -1025,7 +1038,7 @@ hipError_t launch_dtype_kn(const GemmPlan& p, const void* A, const void* B, floa
 #define X(cbm, cbn, cwm, cwn, cnb)                                                \
     if (p.bm == cbm && p.bn == cbn && p.waves == cwm * cwn && p.stages == cwm &&  \
         p.nbuf == cnb)                                                            \
-        return launch_tiled<DT, cbm, cbn, cwm, cwn, cnb, 1>(A, B, P, M, N, K, kps, splits, st);
+        return launch_tiled<DT, cbm, cbn, cwm, cwn, cnb, 1>(A, B, P, M, N, K, kps, splits, p.order, st);
         SPLITK_KN_TILED_CONFIGS(X)
 #undef X
     }
@@ -1054,7 +1067,7 @@ hipError_t launch_dtype(const GemmPlan& p, const void* A, const void* B, float* 
 #define X(cbm, cbn, cwm, cwn, cnb)                                                \
     if (p.bm == cbm && p.bn == cbn && p.waves == cwm * cwn && p.stages == cwm &&  \
         p.nbuf == cnb)                                                            \
-        return launch_tiled<DT, cbm, cbn, cwm, cwn, cnb, 0>(A, B, P, M, N, K, kps, splits, st);
+        return launch_tiled<DT, cbm, cbn, cwm, cwn, cnb, 0>(A, B, P, M, N, K, kps, splits, p.order, st);
         SPLITK_TILED_CONFIGS(X)
 #undef X
     }
@@ -1185,13 +1198,35 @@ static GemmPlan plan_by_shape(int dtype, int64_t M, int64_t N, int64_t K, int64_
 // lost 0.4-11 us, the GEMM slowing by up to 27%.
 constexpr int64_t kSplitFastBytes = int64_t(3) << 20;
 
+// Slabs of a large-tile GEMM up to this size stay in the L2s of the eight
+// XCDs (4 MiB each) until the slab sum reads them.
+constexpr int64_t kTiledLocalSlabBytes = int64_t(32) << 20;
+
 // Tile order of a plan: split fastest where the tile-ordered slab sum
-// applies (a skinny tile of 32x32, 32x64 or 64x64, 2..8 splits, N % 4 == 0)
-// and the operand panels of the tiles on one XCD fit kSplitFastBytes.
-static int tile_order(const GemmPlan& p, int dtype, int64_t M, int64_t N, int64_t K, int64_t splits) {
-    if (p.kind == kTiled || splits < 2 || splits > 8 || N % 4 != 0) return 0;
-    if (!((p.bm == 32 && (p.bn == 32 || p.bn == 64)) || (p.bm == 64 && p.bn == 64))) return 0;
+// applies (2..8 splits, N % 4 == 0) and
+//  - for a skinny tile (32x32, 32x64, 64x64), the operand panels of the
+//    tiles on one XCD fit kSplitFastBytes;
+//  - for a large tile (256x128, 256x256), the grid is one round, the slabs
+//    fit kTiledLocalSlabBytes and a split is at most 12 chunks of K.
+//    Summing every slab on the XCD that wrote it then also spares the next
+//    GEMM, a gain of a few microseconds, while the GEMM loses the panels the
+//    split-major order shares on an XCD, a loss that grows with the split
+//    length.  Measured with 256x128 tiles, GEMM + sum: 3 to 12 chunks
+//    0.65-1.04x the split-major time (20.1 -> 15.9 us for 768x1536x1536 in
+//    4 splits, 22.7 -> 14.7 for 512x1536x1536 in 8), 24 chunks and more
+//    0.96-1.13x (28.2 -> 31.7 for 768x768x12288 in 8 splits); past one
+//    round 34.9 -> 38.3 (1536x1536x3072, 4 splits, 288 workgroups).
+static int tile_order(const GemmPlan& p, int dtype, int64_t M, int64_t N, int64_t K, int64_t kps,
+                      int64_t splits) {
+    if (splits < 2 || splits > 8 || N % 4 != 0) return 0;
     const int64_t es = dtype == 0 ? 4 : 2;
+    if (p.kind == kTiled) {
+        if (!(p.bm == 256 && (p.bn == 128 || p.bn == 256))) return 0;
+        const int64_t chunks = (kps * es + 127) / 128;
+        return p.grid <= device_cus() && splits * M * N * 4 <= kTiledLocalSlabBytes && chunks <= 12
+                   ? 1 : 0;
+    }
+    if (!((p.bm == 32 && (p.bn == 32 || p.bn == 64)) || (p.bm == 64 && p.bn == 64))) return 0;
     const int64_t tiles_m = M / p.bm;
     const int64_t held = 32 / splits > 1 ? 32 / splits : 1;  // tiles per XCD at once, one workgroup per CU
     const int64_t rows = (held < tiles_m ? held : tiles_m) * p.bm + ((held + tiles_m - 1) / tiles_m) * p.bn;
@@ -1201,7 +1236,6 @@ static int tile_order(const GemmPlan& p, int dtype, int64_t M, int64_t N, int64_
 GemmPlan plan_gemm(int dtype, int64_t M, int64_t N, int64_t K, int64_t kps, int64_t splits,
                    int layout) {
     GemmPlan p = plan_by_shape(dtype, M, N, K, kps, splits, layout);
-    p.order = tile_order(p, dtype, M, N, K, splits);
     // With too few 256-row tiles to fill the chip the rules above pick a
     // skinny kernel, but where M allows 256-row tiles the large-tile kernel
     // can still be faster on fewer CUs: each of its workgroups streams about
@@ -1211,8 +1245,9 @@ GemmPlan plan_gemm(int dtype, int64_t M, int64_t N, int64_t K, int64_t kps, int6
         const int64_t tiles = (M / 256) * ((N + 127) / 128) * splits;
         const GemmPlan big{kTiled, 256, 128, 8, 2, tiles, 512, layout, tiled_nbuf(256, 128)};
         if (gemm_cost_us(big, dtype, M, N, K, kps, splits) < gemm_cost_us(p, dtype, M, N, K, kps, splits))
-            return big;
+            p = big;
     }
+    p.order = tile_order(p, dtype, M, N, K, kps, splits);
     return p;
 }
 

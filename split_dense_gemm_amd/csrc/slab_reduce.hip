@@ -228,6 +228,8 @@ hipError_t launch_tiles_out(int bm, int bn, const float* partials, void* C, int 
     if (bm == 32 && bn == 32) return launch_tiles_s<32, 32, OT>(partials, C, s, M, N, st);
     if (bm == 32 && bn == 64) return launch_tiles_s<32, 64, OT>(partials, C, s, M, N, st);
     if (bm == 64 && bn == 64) return launch_tiles_s<64, 64, OT>(partials, C, s, M, N, st);
+    if (bm == 256 && bn == 128) return launch_tiles_s<256, 128, OT>(partials, C, s, M, N, st);
+    if (bm == 256 && bn == 256) return launch_tiles_s<256, 256, OT>(partials, C, s, M, N, st);
     return hipErrorInvalidValue;
 }
 
@@ -237,7 +239,8 @@ hipError_t launch_slab_reduce_after(const GemmPlan& plan, const float* partials,
                                     int64_t splits, int64_t M, int64_t N, int out_dtype,
                                     hipStream_t stream) {
     const bool tile_shape = (plan.bm == 32 && (plan.bn == 32 || plan.bn == 64)) ||
-                            (plan.bm == 64 && plan.bn == 64);
+                            (plan.bm == 64 && plan.bn == 64) ||
+                            (plan.bm == 256 && (plan.bn == 128 || plan.bn == 256));
     if (plan.order == 1 && tile_shape && splits <= 8 && N % 4 == 0 && M % plan.bm == 0) {
         const int s = (int)splits;
         switch (out_dtype) {

@@ -9,11 +9,15 @@
 // runs at call time:
 //
 //   GEMM    t0 + rounds * (a + b * MB staged per wave + c * MB staged per
-//           workgroup), floored by the HBM time of its unique traffic, where
-//           rounds = workgroups / (256 CUs * workgroups resident per CU),
-//           rounded up.  In the skinny kernels a wave's own chunk count sets
-//           the critical path (the waves of a workgroup share the split's
-//           chunks); the large-tile kernels have no per-wave term;
+//           workgroup) + d * MB of partial slabs written, floored by the HBM
+//           time of its unique traffic, where rounds = workgroups / (256 CUs
+//           * workgroups resident per CU), rounded up.  In the skinny kernels
+//           a wave's own chunk count sets the critical path (the waves of a
+//           workgroup share the split's chunks); the large-tile kernels have
+//           no per-wave term, but a slab term: each workgroup stores its
+//           128-256 KiB tile after its last chunk with nothing to overlap,
+//           and the store time grows with how many workgroups store at once,
+//           which a per-round constant cannot follow;
 //   reduce  r0 + bytes moved / bandwidth (+ one more load round past eight
 //           slabs); absent when one split writes C directly.
 //
@@ -21,7 +25,11 @@
 // MI355X times of each (kernel family, element size): 480 BF16 shapes (M
 // 32..4096, N 512..8192, K 1024..16384, including a dense grid of the small
 // shapes M 32..320, N 512..1536, K 1024..6144) and 45 F32 shapes, each at
-// all five split counts.  Candidates that are not powers of two (3, 6, 12)
+// all five split counts.  The 16-bit large-tile rows are fitted on the whole
+// operation instead (GEMM + slab sum, less the modelled sum): 64 BF16 shapes
+// (M 256, 512, 1024, 2048; N 768..6144; K 1536..12288) at all five split
+// counts, each with the shape rules' kernel and with the 256x128 kernel
+// forced, which is where the two families compete.  Candidates that are not powers of two (3, 6, 12)
 // never won in those measurements and are not considered.
 #include <math.h>
 #include <stdint.h>
@@ -42,15 +50,17 @@ struct Coef {
     double t0, a;  // microseconds
     double b;      // per MB staged by one wave (skinny kernels)
     double c;      // per MB staged by one workgroup
+    double d;      // per MB of partial slabs written (large-tile kernels)
 };
 
 // [element size 2 or 4][family]: skinny with DMA tail, skinny, tiled 256x128, tiled 256x256.
-// The 256x128 family was fitted on its 2x2-wave kernel; the 2x4-wave kernel
-// that replaced it measured ~6% faster on eight shapes, applied as a factor.
-constexpr Coef kCoef16[4] = {{0.701, 1.510, 62.80, 5.154}, {-0.275, 2.723, 2.126, 11.14},
-                             {3.663, 3.663, 0.0, 21.25}, {0.912, 10.67, 0.0, 28.71}};
-constexpr Coef kCoef32[4] = {{0.543, 1.120, 140.1, 14.27}, {-2.394, 4.521, 2.831, 22.65},
-                             {3.854, 3.854, 0.0, 87.00}, {1.636, 10.39, 0.0, 122.1}};
+// The F32 large-tile rows carry no slab term: they come from GEMM-alone
+// times, the 256x128 one from the earlier 2x2-wave kernel with the ~6% that
+// the 2x4-wave kernel gained on eight shapes applied as a factor.
+constexpr Coef kCoef16[4] = {{0.701, 1.510, 62.80, 5.154, 0.0}, {-0.275, 2.723, 2.126, 11.14, 0.0},
+                             {3.931, -1.702, 0.0, 14.46, 0.201}, {-0.844, 1.284, 0.0, 23.47, 0.136}};
+constexpr Coef kCoef32[4] = {{0.543, 1.120, 140.1, 14.27, 0.0}, {-2.394, 4.521, 2.831, 22.65, 0.0},
+                             {3.854, 3.854, 0.0, 87.00, 0.0}, {1.636, 10.39, 0.0, 122.1, 0.0}};
 
 // Workgroups of one configuration resident on a CU at once, from each
 // kernel's LDS use (160 KiB per CU) and VGPR use (512 per lane per SIMD).
@@ -84,8 +94,10 @@ double gemm_cost_us(const GemmPlan& p, int dtype, int64_t M, int64_t N, int64_t 
     const double chunk_mb = (double)(p.bm + p.bn) * 128.0 / 1e6;
     const double per_wave = p.kind == kTiled ? 0.0 : (double)((chunks + p.waves - 1) / p.waves) * chunk_mb;
     const Coef& c = coef_of(p, es);
-    const double t = c.t0 + rounds * (c.a + c.b * per_wave + c.c * (double)chunks * chunk_mb);
-    const double hbm = ((double)(M + N) * (double)K * es + (double)splits * M * N * 4) / kHbmBytesPerUs;
+    const double slab_bytes = (double)splits * M * N * 4;
+    const double t = c.t0 + rounds * (c.a + c.b * per_wave + c.c * (double)chunks * chunk_mb) +
+                     c.d * slab_bytes / 1e6;
+    const double hbm = ((double)(M + N) * (double)K * es + slab_bytes) / kHbmBytesPerUs;
     return fmax(t, kHbmFloorUs + hbm);
 }
 

@@ -123,8 +123,9 @@ int describe_plan(int layout, int64_t M, int64_t N, int64_t K, int64_t k_per_spl
     const splitk::GemmPlan p = splitk::plan_gemm(dtype, M, N, K, k_per_split, splits, layout);
     if (buf && len > 0) {
         if (p.kind == splitk::kTiled)
-            snprintf(buf, (size_t)len, "tiled bm%d bn%d waves%dx%d ring%d block%d grid%lld", p.bm, p.bn,
-                     p.stages, p.waves / p.stages, p.nbuf, p.block, (long long)p.grid);
+            snprintf(buf, (size_t)len, "tiled bm%d bn%d waves%dx%d ring%d block%d grid%lld%s", p.bm, p.bn,
+                     p.stages, p.waves / p.stages, p.nbuf, p.block, (long long)p.grid,
+                     p.order == 1 ? " splitfast" : "");
         else
             snprintf(buf, (size_t)len, "%s bm%d bn%d waves%d stages%d block%d grid%lld%s",
                      p.kind == splitk::kWaveKDma ? "wavekdma" : "wavek", p.bm, p.bn, p.waves, p.stages,

@@ -195,3 +195,54 @@ def test_tiled_multi_round_exact(hip_lib, case):
     assert np.all(c[M * N:].view(np.uint32) == guard)
     np.testing.assert_array_equal(p[: S * M * N].astype(np.float64), EP.reshape(-1))
     np.testing.assert_array_equal(c[: M * N].astype(np.float64), EC.reshape(-1))
+
+
+# Large-tile configurations on one round of workgroups with few slabs: every
+# split of a tile runs on one XCD (split fastest) and the slab sum takes each
+# tile on that XCD.  Tile counts of 12 and 9 per split (one a multiple of 8
+# XCDs' worth of tiles, one not), a 40-column last tile, 2, 5 and 8 splits,
+# F32 and rounded BF16 / F16 outputs.  Exact-arithmetic inputs: the partials
+# and C match the binary64 reference bit for bit (C rounded once).
+SPLIT_FAST = [(cfg, S, out, tm) for cfg in TILED if cfg[:2] in ((256, 128), (256, 256))
+              for S, out, tm in ((2, "f32", 3), (5, "bf16", 3), (8, "f16", 2), (8, "f32", 3))]
+
+
+@pytest.mark.gpu
+@pytest.mark.skipif(not gpu_available(), reason="no GPU")
+@pytest.mark.parametrize("case", SPLIT_FAST,
+                         ids=lambda c: "tiled," + ",".join(map(str, c[0])) + f"-S{c[1]}-{c[2]}-tm{c[3]}")
+def test_tiled_split_fastest_exact(hip_lib, case):
+    cfg, S, out, tm = case
+    bm, bn = cfg[0], cfg[1]
+    M, N, kps = tm * bm, 2 * bn + 40, 96
+    K = (S - 1) * kps + 64
+    dtype = "bf16"
+    old = os.environ.get("SPLITK_PLAN")
+    os.environ["SPLITK_PLAN"] = _plan_text("tiled", cfg)
+    try:
+        text = hip_lib.describe(M, N, K, kps, S, inputs.DTYPES[dtype])
+        print(f"case {dtype}->{out} M{M} N{N} K{K} kps{kps} S{S}: {text}", flush=True)
+        assert f"bm{bm} bn{bn}" in text and text.endswith("splitfast"), text
+        dev = torch.device("cuda:0")
+        ea, eb = inputs.exact_operands(M, N, K, dtype, seed=bm + bn + S + tm)
+        ea64 = oracle.decode(inputs.stored_bits(ea), dtype)
+        eb64 = oracle.decode(inputs.stored_bits(eb), dtype)
+        EP, _, _ = oracle.splitk_partials(ea64, eb64, kps, S)
+        EC = oracle.encode(EP.sum(axis=0), out).ravel()
+        pbuf = inputs.guarded_buffer(S * M * N, "nan").to(dev)
+        cbuf = inputs.guarded_buffer(M * N, "nan", dtype=out).to(dev)
+        hip_lib.gemm_bt_reduce(ea.to(dev), eb.to(dev), pbuf[: S * M * N].view(S, M, N),
+                               cbuf[: M * N].view(M, N), kps, S)
+        torch.cuda.synchronize()
+        p, c = pbuf.cpu().numpy(), inputs.stored_bits(cbuf.cpu())
+    finally:
+        if old is None:
+            os.environ.pop("SPLITK_PLAN", None)
+        else:
+            os.environ["SPLITK_PLAN"] = old
+    guard = np.float32(inputs.GUARD_VALUE).view(np.uint32)
+    assert np.all(p[S * M * N:].view(np.uint32) == guard)
+    np.testing.assert_array_equal(p[: S * M * N].astype(np.float64), EP.reshape(-1))
+    np.testing.assert_array_equal(c[: M * N], EC)
+    guard_c = inputs.stored_bits(inputs.guarded_buffer(0, "nan", dtype=out))
+    assert np.all(c[M * N:] == guard_c)

@@ -10,7 +10,8 @@ slabs in ascending s in F32), for every output type, with NaN-poisoned
 outputs fully overwritten and the 64 guards intact.  Geometries cover both
 small tile shapes, a forced 64x64 tile, tile counts that are and are not
 multiples of the 8 XCDs, column tails, and the cases that fall back to the
-flat order (N % 4 != 0, more than eight slabs, large-tile GEMMs).
+flat order (N % 4 != 0, more than eight slabs, large-tile GEMMs past one
+round of workgroups or 32 MiB of slabs).
 """
 from __future__ import annotations
 
@@ -42,7 +43,8 @@ GEOMETRIES = [
     (64, 768, 12288, 1536, 8, "bf16", None, False),    # long K: split-major order, flat pass
     (64, 130, 512, 256, 2, "bf16", None, False),       # N % 4 != 0: flat order
     (32, 64, 2048, 128, 16, "bf16", None, False),      # sixteen slabs: flat order
-    (2048, 2048, 1024, 512, 2, "bf16", None, False),   # large-tile GEMM: flat order
+    (2048, 2048, 1024, 512, 2, "bf16", None, True),    # 256x128 tiles, one round, 32 MiB of slabs
+    (2048, 4096, 1024, 512, 2, "bf16", None, False),   # large tiles, 64 MiB of slabs: flat order
 ]
 
 

@@ -201,18 +201,21 @@ def test_tiled_multi_round_exact(hip_lib, case):
 # split of a tile runs on one XCD (split fastest) and the slab sum takes each
 # tile on that XCD.  Tile counts of 12 and 9 per split (one a multiple of 8
 # XCDs' worth of tiles, one not), a 40-column last tile, 2, 5 and 8 splits,
-# F32 and rounded BF16 / F16 outputs.  Exact-arithmetic inputs: the partials
-# and C match the binary64 reference bit for bit (C rounded once).
-SPLIT_FAST = [(cfg, S, out, tm) for cfg in TILED if cfg[:2] in ((256, 128), (256, 256))
+# F32 and rounded BF16 / F16 outputs, both B layouts.  Exact-arithmetic
+# inputs: the partials and C match the binary64 reference bit for bit (C
+# rounded once).
+SPLIT_FAST = [(layout, cfg, S, out, tm)
+              for layout, cfgs in (("nk", TILED), ("kn", KN_TILED))
+              for cfg in cfgs if cfg[:2] in ((256, 128), (256, 256))
               for S, out, tm in ((2, "f32", 3), (5, "bf16", 3), (8, "f16", 2), (8, "f32", 3))]
 
 
 @pytest.mark.gpu
 @pytest.mark.skipif(not gpu_available(), reason="no GPU")
 @pytest.mark.parametrize("case", SPLIT_FAST,
-                         ids=lambda c: "tiled," + ",".join(map(str, c[0])) + f"-S{c[1]}-{c[2]}-tm{c[3]}")
+                         ids=lambda c: f"{c[0]}:tiled," + ",".join(map(str, c[1])) + f"-S{c[2]}-{c[3]}-tm{c[4]}")
 def test_tiled_split_fastest_exact(hip_lib, case):
-    cfg, S, out, tm = case
+    layout, cfg, S, out, tm = case
     bm, bn = cfg[0], cfg[1]
     M, N, kps = tm * bm, 2 * bn + 40, 96
     K = (S - 1) * kps + 64
@@ -220,9 +223,12 @@ def test_tiled_split_fastest_exact(hip_lib, case):
     old = os.environ.get("SPLITK_PLAN")
     os.environ["SPLITK_PLAN"] = _plan_text("tiled", cfg)
     try:
-        text = hip_lib.describe(M, N, K, kps, S, inputs.DTYPES[dtype])
-        print(f"case {dtype}->{out} M{M} N{N} K{K} kps{kps} S{S}: {text}", flush=True)
+        describe = hip_lib.describe if layout == "nk" else hip_lib.describe_bn
+        text = describe(M, N, K, kps, S, inputs.DTYPES[dtype])
+        print(f"case {layout} {dtype}->{out} M{M} N{N} K{K} kps{kps} S{S}: {text}", flush=True)
         assert f"bm{bm} bn{bn}" in text and text.endswith("splitfast"), text
+        stored = (lambda t: t) if layout == "nk" else (lambda t: t.T.contiguous())
+        gemm_reduce = hip_lib.gemm_bt_reduce if layout == "nk" else hip_lib.gemm_bn_reduce
         dev = torch.device("cuda:0")
         ea, eb = inputs.exact_operands(M, N, K, dtype, seed=bm + bn + S + tm)
         ea64 = oracle.decode(inputs.stored_bits(ea), dtype)
@@ -231,8 +237,8 @@ def test_tiled_split_fastest_exact(hip_lib, case):
         EC = oracle.encode(EP.sum(axis=0), out).ravel()
         pbuf = inputs.guarded_buffer(S * M * N, "nan").to(dev)
         cbuf = inputs.guarded_buffer(M * N, "nan", dtype=out).to(dev)
-        hip_lib.gemm_bt_reduce(ea.to(dev), eb.to(dev), pbuf[: S * M * N].view(S, M, N),
-                               cbuf[: M * N].view(M, N), kps, S)
+        gemm_reduce(ea.to(dev), stored(eb).to(dev), pbuf[: S * M * N].view(S, M, N),
+                    cbuf[: M * N].view(M, N), kps, S)
         torch.cuda.synchronize()
         p, c = pbuf.cpu().numpy(), inputs.stored_bits(cbuf.cpu())
     finally:

@@ -25,11 +25,12 @@
 // MI355X times of each (kernel family, element size): 480 BF16 shapes (M
 // 32..4096, N 512..8192, K 1024..16384, including a dense grid of the small
 // shapes M 32..320, N 512..1536, K 1024..6144) and 45 F32 shapes, each at
-// all five split counts.  The 16-bit large-tile rows are fitted on the whole
-// operation instead (GEMM + slab sum, less the modelled sum): 64 BF16 shapes
-// (M 256, 512, 1024, 2048; N 768..6144; K 1536..12288) at all five split
-// counts, each with the shape rules' kernel and with the 256x128 kernel
-// forced, which is where the two families compete.  Candidates that are not powers of two (3, 6, 12)
+// all five split counts.  The large-tile rows are fitted on the whole
+// operation instead (GEMM + slab sum, less the modelled sum), at all five
+// split counts, each shape with the shape rules' kernel and with the 256x128
+// kernel forced, which is where the families compete: 64 BF16 shapes (M 256,
+// 512, 1024, 2048; N 768..6144; K 1536..12288) and 20 F32 shapes (M 32..2048,
+// N 1024 and 4096, K 2048 and 8192).  Candidates that are not powers of two (3, 6, 12)
 // never won in those measurements and are not considered.
 #include <math.h>
 #include <stdint.h>
@@ -54,13 +55,10 @@ struct Coef {
 };
 
 // [element size 2 or 4][family]: skinny with DMA tail, skinny, tiled 256x128, tiled 256x256.
-// The F32 large-tile rows carry no slab term: they come from GEMM-alone
-// times, the 256x128 one from the earlier 2x2-wave kernel with the ~6% that
-// the 2x4-wave kernel gained on eight shapes applied as a factor.
 constexpr Coef kCoef16[4] = {{0.701, 1.510, 62.80, 5.154, 0.0}, {-0.275, 2.723, 2.126, 11.14, 0.0},
                              {3.931, -1.702, 0.0, 14.46, 0.201}, {-0.844, 1.284, 0.0, 23.47, 0.136}};
 constexpr Coef kCoef32[4] = {{0.543, 1.120, 140.1, 14.27, 0.0}, {-2.394, 4.521, 2.831, 22.65, 0.0},
-                             {3.854, 3.854, 0.0, 87.00, 0.0}, {1.636, 10.39, 0.0, 122.1, 0.0}};
+                             {4.785, -0.551, 0.0, 76.71, 0.164}, {2.986, 0.0, 0.0, 114.4, 0.129}};
 
 // Workgroups of one configuration resident on a CU at once, from each
 // kernel's LDS use (160 KiB per CU) and VGPR use (512 per lane per SIMD).

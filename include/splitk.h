@@ -128,10 +128,12 @@ int splitk_reduce_typed(const float* partials, void* C, int64_t splits, int64_t 
  * splits, dtype).  The result is the same sum, bit for bit (first page,
  * "Contract and correctness": the separate elementwise accumulation); only
  * the order in which workgroups visit the plane differs.  Where the GEMM
- * ran a small-tile kernel with all the splits of a tile on one XCD, each
- * workgroup takes one output tile and runs on the XCD that wrote that
- * tile's slabs, so it reads them from that XCD's L2 instead of from memory;
- * otherwise it is the flat pass.  The fused calls run this pass.
+ * ran with all the splits of a tile on one XCD (small tiles whose operand
+ * panels fit that XCD's L2; 256-row tiles on a grid of one round with at
+ * most 32 MiB of slabs and short splits), each workgroup takes one output
+ * tile, or one band of it, and runs on the XCD that wrote that tile's slabs,
+ * so it reads them from that XCD's L2 instead of from memory; otherwise it
+ * is the flat pass.  The fused calls run this pass.
  *   partials, C, out_dtype   as for splitk_reduce_typed.
  *   K, k_per_split, dtype    the GEMM's, checked as for splitk_gemm_bt.
  * Returns the statuses of splitk_reduce_typed and of splitk_gemm_bt's shape

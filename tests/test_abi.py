@@ -10,6 +10,7 @@ GPU is present, and the GPU tests cover the same statuses with real buffers.
 from __future__ import annotations
 
 import ctypes
+import os
 
 import pytest
 
@@ -257,6 +258,32 @@ def test_tile_order_choice(hip_lib):
         assert hip_lib.describe(*shape, BF16).endswith(" splitfast"), shape
     for shape in major:
         assert "splitfast" not in hip_lib.describe(*shape, BF16), shape
+
+
+def test_large_tile_order_choice(hip_lib):
+    """256-row tiles take the split-fastest order only on a grid of one round
+    (at most 256 workgroups on 256 CUs) with at most 32 MiB of slabs and at
+    most 12 chunks of 128 bytes per split, for both B layouts."""
+    tiled = "SPLITK_PLAN"
+    fast = [(768, 1536, 1536, 384, 4), (512, 1536, 1536, 192, 8), (2048, 2048, 1024, 512, 2),
+            (768, 3072, 1536, 768, 2)]
+    major = [(768, 768, 12288, 1536, 8),    # 24 chunks per split
+             (1536, 1536, 3072, 768, 4),    # 288 workgroups
+             (2048, 4096, 1024, 512, 2),    # 64 MiB of slabs
+             (768, 1536, 1536, 96, 16)]     # more than eight splits
+    assert tiled not in os.environ
+    for describe in (hip_lib.describe, hip_lib.describe_bn):
+        for shape in fast:
+            text = describe(*shape, BF16)
+            assert text.startswith("tiled bm256") and text.endswith(" splitfast"), (shape, text)
+        for shape in major:
+            text = describe(*shape, BF16)
+            assert text.startswith("tiled bm256") and "splitfast" not in text, (shape, text)
+    # F32: 32 elements per chunk, so 384 per split is 12 chunks and 416 is 13.
+    text = hip_lib.describe(768, 1536, 1536, 384, 4, 0)
+    assert text.startswith("tiled bm256") and text.endswith(" splitfast"), text
+    text = hip_lib.describe(768, 1536, 1664, 416, 4, 0)
+    assert text.startswith("tiled bm256") and "splitfast" not in text, text
 
 
 @pytest.mark.parametrize("args,status", SHAPE_CASES)

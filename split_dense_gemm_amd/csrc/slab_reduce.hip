@@ -148,9 +148,10 @@ hipError_t launch_out(const float* partials, void* C, int s, int64_t plane4, hip
 // Row bands per tile in the tile-ordered pass: one 16-byte word per lane.
 constexpr int tile_bands(int bm, int bn) { return bm * bn / (4 * kBlock) > 1 ? bm * bn / (4 * kBlock) : 1; }
 
-// Tile-ordered pass for the slabs of a skinny GEMM (BM x BN output tiles,
-// tiles_m of them down M).  Each tile is split into PT row bands of one
-// 16-byte word per lane; workgroup b takes band lr % PT of tile
+// Tile-ordered pass for the slabs of a GEMM in the split-fastest order (BM x
+// BN output tiles, tiles_m of them down M: the skinny tiles, and 256x128 or
+// 256x256 tiles on a grid of one round).  Each tile is split into PT row
+// bands of one 16-byte word per lane; workgroup b takes band lr % PT of tile
 // u = lr / PT, lr = xcd_logical_id(b, n):
 // the GEMM wrote every slab of tile u from the workgroups of one XCD (split
 // fastest, each XCD a contiguous range of logical ids), and when the number

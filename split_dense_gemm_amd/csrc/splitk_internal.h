@@ -32,7 +32,7 @@ struct GemmPlan {
     int block;     // threads per workgroup
     int layout;    // BLayout of B
     int nbuf = 0;  // tiled kernels: chunk buffers in the LDS ring (0: the tile's default)
-    int order = 0; // skinny kernels: 1 = splits of a tile on one XCD (see skinny_tile)
+    int order = 0; // 1 = splits of a tile on one XCD (skinny_tile; the large-tile kernel's tile order)
 };
 
 // Renumbers workgroups so that consecutive logical ids run on one XCD.
@@ -101,9 +101,9 @@ hipError_t launch_slab_reduce(const float* partials, void* C, int64_t splits, in
                               int out_dtype, hipStream_t stream);
 
 // The same sum for slabs that the GEMM `plan` has just written: after a
-// skinny GEMM in the split-fastest order (plan.order == 1) each workgroup
-// takes one output tile, on the XCD whose L2 holds that tile's slabs;
-// otherwise the flat pass above.
+// GEMM in the split-fastest order (plan.order == 1) each workgroup takes one
+// output tile, or one band of it, on the XCD whose L2 holds that tile's
+// slabs; otherwise the flat pass above.
 hipError_t launch_slab_reduce_after(const GemmPlan& plan, const float* partials, void* C,
                                     int64_t splits, int64_t M, int64_t N, int out_dtype,
                                     hipStream_t stream);

@@ -1156,9 +1156,23 @@ static GemmPlan plan_by_shape(int dtype, int64_t M, int64_t N, int64_t K, int64_
     // 5-8% faster than 2x2 for this tile); these read the least L2 data per
     // flop.  An N that 256 does not divide takes 256x128 tiles, the last one
     // a tail.
-    if (M % 256 == 0 && N % 256 == 0 && (M / 256) * (N / 256) * splits >= 256)
-        return GemmPlan{kTiled, 256, 256, 4, 2, (M / 256) * (N / 256) * splits, 256, layout,
-                        tiled_nbuf(256, 256)};
+    //
+    // With B as [N,K] in one or two splits, 256x128 tiles also take over
+    // where 256x256 ones would fill one round and at most half of a second
+    // (257-384 workgroups on 256 CUs): twice the workgroups at half the work
+    // each end half a round earlier.  Measured, GEMM + sum: BF16 0.87-0.90x
+    // (4096x4608x4096 in one split 172.0 -> 149.9 us, 3072x6144x1536
+    // 80.6 -> 69.5), F16 0.90-0.91x, F32 0.77-0.79x.  Further out the gain
+    // shrinks and long splits reverse it (3072x6144x12288 in four splits,
+    // 1152 workgroups: 452.6 -> 527.9 us), and the split-count model ranks
+    // 256x128 plans of many splits too cheaply.  With B as [K,N] the
+    // 256x128 kernel was 3-7% slower on four such grids, and 256x256 stays.
+    if (M % 256 == 0 && N % 256 == 0 && (M / 256) * (N / 256) * splits >= 256) {
+        const int64_t wg = (M / 256) * (N / 256) * splits;
+        const bool short_last_round = layout == kLayoutNK && splits <= 2 && wg > 256 && wg <= 384;
+        if (!short_last_round)
+            return GemmPlan{kTiled, 256, 256, 4, 2, wg, 256, layout, tiled_nbuf(256, 256)};
+    }
     if (M % 256 == 0 && (M / 256) * cdiv(N, 128) * splits >= 256)
         return GemmPlan{kTiled, 256, 128, 8, 2, (M / 256) * cdiv(N, 128) * splits, 512, layout,
                         tiled_nbuf(256, 128)};

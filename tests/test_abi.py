@@ -310,3 +310,23 @@ def test_bn_pointer_checks_without_device(hip_lib):
     assert red(A_PTR, B_PTR, P_PTR, None, 256, 1024, 2048, 1024, 2, BF16, 0, None) == NULL
     assert red(A_PTR, B_PTR, P_PTR, C_PTR, 256, 1024, 2048, 1024, 2, BF16, 4, None) == DTYPE
     assert red(A_PTR, B_PTR, P_PTR, A_PTR, 256, 1024, 2048, 1024, 2, BF16, 0, None) == ALIAS
+
+
+def test_short_last_round_takes_256x128_tiles(hip_lib):
+    """With B as [N,K] in one or two splits, 256x128 tiles replace 256x256
+    ones where these would be 257-384 workgroups (one round and at most half
+    of another on 256 CUs).  Other counts, more splits, and B as [K,N] keep
+    256x256 tiles."""
+    half = [(4096, 4608, 4096, 4096, 1), (3072, 6144, 1536, 1536, 1), (2048, 6144, 3072, 1536, 2)]
+    full = [(2048, 4096, 4096, 512, 8), (4096, 4096, 8192, 2048, 4), (2048, 7168, 2048, 1024, 2),
+            (3072, 6144, 12288, 3072, 4), (768, 3072, 12288, 1536, 8), (4096, 4096, 4096, 4096, 1)]
+    for shape in half:
+        wg = (shape[0] // 256) * (shape[1] // 256) * shape[4]
+        assert 256 < wg <= 384 and shape[4] <= 2, shape
+        assert hip_lib.describe(*shape, BF16).startswith(f"tiled bm256 bn128 waves2x4 ring3 block512 grid{2 * wg}")
+        assert hip_lib.describe_bn(*shape, BF16).startswith(f"tiled bm256 bn256 waves2x2 ring2 block256 grid{wg}")
+    for shape in full:
+        wg = (shape[0] // 256) * (shape[1] // 256) * shape[4]
+        assert not (256 < wg <= 384 and shape[4] <= 2), shape
+        for describe in (hip_lib.describe, hip_lib.describe_bn):
+            assert describe(*shape, BF16).startswith(f"tiled bm256 bn256 waves2x2 ring2 block256 grid{wg}")

@@ -313,10 +313,10 @@ def test_bn_pointer_checks_without_device(hip_lib):
 
 
 def test_short_last_round_takes_256x128_tiles(hip_lib):
-    """With B as [N,K] in one or two splits, 256x128 tiles replace 256x256
-    ones where these would be 257-384 workgroups (one round and at most half
-    of another on 256 CUs).  Other counts, more splits, and B as [K,N] keep
-    256x256 tiles."""
+    """With B as [N,K], 256x128 tiles replace 256x256 ones where the last
+    round of 256x256 workgroups would be at most half full: for 16-bit inputs
+    only in one or two splits with 257-384 workgroups, for F32 at any split
+    count.  Other counts and B as [K,N] keep 256x256 tiles."""
     half = [(4096, 4608, 4096, 4096, 1), (3072, 6144, 1536, 1536, 1), (2048, 6144, 3072, 1536, 2)]
     full = [(2048, 4096, 4096, 512, 8), (4096, 4096, 8192, 2048, 4), (2048, 7168, 2048, 1024, 2),
             (3072, 6144, 12288, 3072, 4), (768, 3072, 12288, 1536, 8), (4096, 4096, 4096, 4096, 1)]
@@ -330,3 +330,10 @@ def test_short_last_round_takes_256x128_tiles(hip_lib):
         assert not (256 < wg <= 384 and shape[4] <= 2), shape
         for describe in (hip_lib.describe, hip_lib.describe_bn):
             assert describe(*shape, BF16).startswith(f"tiled bm256 bn256 waves2x2 ring2 block256 grid{wg}")
+    # F32: any split count, wherever the last 256x256 round is at most half full.
+    for shape, wg in (((3072, 3072, 6144, 768, 8), 1152), ((3072, 3072, 3072, 768, 4), 576)):
+        assert hip_lib.describe(*shape, 0).startswith(f"tiled bm256 bn128 waves2x4 ring3 block512 grid{2 * wg}")
+        assert hip_lib.describe_bn(*shape, 0).startswith(f"tiled bm256 bn256 waves2x2 ring2 block256 grid{wg}")
+        assert hip_lib.describe(*shape, BF16).startswith(f"tiled bm256 bn256 waves2x2 ring2 block256 grid{wg}")
+    # F32 on whole rounds (512 workgroups) keeps 256x256 tiles.
+    assert hip_lib.describe(2048, 4096, 4096, 1024, 4, 0).startswith("tiled bm256 bn256 waves2x2 ring2 block256 grid512")

@@ -1162,19 +1162,24 @@ static GemmPlan plan_by_shape(int dtype, int64_t M, int64_t N, int64_t K, int64_
     // 1..128): twice the workgroups at half the work each end half a round
     // earlier.  F32, GEMM + sum: 0.78x at 288 workgroups (2048x4608x4096 in
     // two splits 973.5 -> 757.5 us), 0.85-0.88x at 576, 0.93x at 1152; on
-    // whole rounds 256x256 stays 1-7% faster.  16-bit inputs gain less and
-    // only in one or two splits with 257-384 workgroups: BF16 0.87-0.90x
+    // whole rounds 256x256 stays 1-7% faster.  16-bit inputs gain less:
+    // BF16 0.87-0.90x at 257-384 workgroups in one or two splits
     // (4096x4608x4096 in one split 172.0 -> 149.9 us, 3072x6144x1536
-    // 80.6 -> 69.5), F16 0.90-0.91x.  Further out their gain shrinks and
-    // long splits reverse it (3072x6144x12288 in four splits, 1152
-    // workgroups: 452.6 -> 527.9 us), and the split-count model ranks such
-    // 256x128 plans of many splits too cheaply.  With B as [K,N] the 256x128
-    // kernel was 3-7% slower on four such grids, and 256x256 stays.
+    // 80.6 -> 69.5), F16 0.90-0.91x; further out only with short splits,
+    // since long ones reverse it (3072x6144x12288 in four splits, 1152
+    // workgroups: 452.6 -> 527.9 us) and the split-count model ranks such
+    // 256x128 plans of many splits too cheaply.  So 16-bit inputs switch in
+    // one or two splits up to 384 workgroups, or with at most 12 chunks per
+    // split.  Over 200 BF16 (shape, split) pairs this takes the time from
+    // 1.049 to 1.011x the faster of the two tiles at geometric mean.  With
+    // B as [K,N] the 256x128 kernel was 3-7% slower on four such grids, and
+    // 256x256 stays.
     if (M % 256 == 0 && N % 256 == 0 && (M / 256) * (N / 256) * splits >= 256) {
         const int64_t wg = (M / 256) * (N / 256) * splits;
         const bool half_round = wg % 256 != 0 && wg % 256 <= 128;
         const bool short_last_round =
-            layout == kLayoutNK && half_round && (dtype == 0 || (splits <= 2 && wg <= 384));
+            layout == kLayoutNK && half_round &&
+            (dtype == 0 || (splits <= 2 && wg <= 384) || max_chunks <= 12);
         if (!short_last_round)
             return GemmPlan{kTiled, 256, 256, 4, 2, wg, 256, layout, tiled_nbuf(256, 256)};
     }

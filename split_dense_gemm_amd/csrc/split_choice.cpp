@@ -54,11 +54,17 @@ struct Coef {
     double d;      // per MB of partial slabs written (large-tile kernels)
 };
 
-// [element size 2 or 4][family]: skinny with DMA tail, skinny, tiled 256x128, tiled 256x256.
-constexpr Coef kCoef16[4] = {{0.701, 1.510, 62.80, 5.154, 0.0}, {-0.275, 2.723, 2.126, 11.14, 0.0},
-                             {3.931, -1.702, 0.0, 14.46, 0.201}, {-0.844, 1.284, 0.0, 23.47, 0.136}};
-constexpr Coef kCoef32[4] = {{0.543, 1.120, 140.1, 14.27, 0.0}, {-2.394, 4.521, 2.831, 22.65, 0.0},
-                             {4.785, -0.551, 0.0, 76.71, 0.164}, {2.986, 0.0, 0.0, 114.4, 0.129}};
+// [element size 2 or 4][family]: skinny with DMA tail, skinny, tiled 256x128,
+// tiled 256x256, tiled 128x128.  The F32 128x128 row is fitted on 30 F32
+// shapes (M 1024-3072, N 1536-6144, K 2048 and 8192) at 1, 2 and 4 splits;
+// 16-bit inputs reach 128x128 tiles only through the override and are priced
+// as 256x128.
+constexpr Coef kCoef16[5] = {{0.701, 1.510, 62.80, 5.154, 0.0}, {-0.275, 2.723, 2.126, 11.14, 0.0},
+                             {3.931, -1.702, 0.0, 14.46, 0.201}, {-0.844, 1.284, 0.0, 23.47, 0.136},
+                             {3.931, -1.702, 0.0, 14.46, 0.201}};
+constexpr Coef kCoef32[5] = {{0.543, 1.120, 140.1, 14.27, 0.0}, {-2.394, 4.521, 2.831, 22.65, 0.0},
+                             {4.785, -0.551, 0.0, 76.71, 0.164}, {2.986, 0.0, 0.0, 114.4, 0.129},
+                             {6.445, -5.188, 0.0, 61.02, 0.478}};
 
 // Workgroups of one configuration resident on a CU at once, from each
 // kernel's LDS use (160 KiB per CU) and VGPR use (512 per lane per SIMD).
@@ -77,6 +83,7 @@ const Coef& coef_of(const GemmPlan& p, int64_t es) {
     const Coef* table = es == 2 ? kCoef16 : kCoef32;
     if (p.kind == kWaveKDma) return table[0];
     if (p.kind == kWaveK) return table[1];
+    if (p.bm == 128 && p.bn == 128) return table[4];
     return (p.bm == 256 && p.bn == 256) ? table[3] : table[2];
 }
 

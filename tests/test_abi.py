@@ -316,8 +316,8 @@ def test_short_last_round_takes_256x128_tiles(hip_lib):
     """With B as [N,K], 256x128 tiles replace 256x256 ones where the last
     round of 256x256 workgroups would be at most half full: for 16-bit inputs
     in one or two splits with 257-384 workgroups or with at most 12 chunks
-    per split, for F32 always.  Other counts and B as [K,N] keep 256x256
-    tiles."""
+    per split.  F32 takes the tile that packs the rounds best, 128x128
+    included.  Other counts and B as [K,N] keep 256x256 tiles."""
     half = [(4096, 4608, 4096, 4096, 1), (3072, 6144, 1536, 1536, 1), (2048, 6144, 3072, 1536, 2)]
     full = [(2048, 4096, 4096, 512, 8), (4096, 4096, 8192, 2048, 4), (2048, 7168, 2048, 1024, 2),
             (3072, 6144, 12288, 3072, 4), (768, 3072, 12288, 1536, 8), (4096, 4096, 4096, 4096, 1)]
@@ -331,15 +331,18 @@ def test_short_last_round_takes_256x128_tiles(hip_lib):
         assert not (256 < wg <= 384 and shape[4] <= 2), shape
         for describe in (hip_lib.describe, hip_lib.describe_bn):
             assert describe(*shape, BF16).startswith(f"tiled bm256 bn256 waves2x2 ring2 block256 grid{wg}")
-    # F32: any split count, wherever the last 256x256 round is at most half
-    # full (here 48 F32 chunks per split; the same splits in BF16 are 24
-    # chunks and keep 256x256 tiles).
-    for shape, wg in (((3072, 3072, 12288, 1536, 8), 1152), ((3072, 3072, 6144, 1536, 4), 576)):
-        assert hip_lib.describe(*shape, 0).startswith(f"tiled bm256 bn128 waves2x4 ring3 block512 grid{2 * wg}")
+    # F32: the tile with the fewest rounds x tile area x per-tile factor
+    # (256x256 1, 256x128 1.05, 128x128 1.1) among the three; the same
+    # shapes in BF16 (24 chunks per split) and B as [K,N] keep 256x256 tiles.
+    f32 = [((3072, 3072, 12288, 1536, 8), "bm256 bn128 waves2x4 ring3 block512 grid2304", 1152),
+           ((3072, 3072, 6144, 1536, 4), "bm128 bn128 waves2x2 ring4 block256 grid2304", 576),
+           ((2048, 4096, 4096, 1024, 4), "bm256 bn256 waves2x2 ring2 block256 grid512", 512)]
+    for shape, plan, wg in f32:
+        assert hip_lib.describe(*shape, 0) == f"tiled {plan}", shape
         assert hip_lib.describe_bn(*shape, 0).startswith(f"tiled bm256 bn256 waves2x2 ring2 block256 grid{wg}")
         assert hip_lib.describe(*shape, BF16).startswith(f"tiled bm256 bn256 waves2x2 ring2 block256 grid{wg}")
+    # F32 on 288 256x128 workgroups (144 256x256 ones): 128x128 tiles.
+    assert hip_lib.describe(2048, 4608, 8192, 8192, 1, 0) == "tiled bm128 bn128 waves2x2 ring4 block256 grid576"
     # 16-bit, 1152 workgroups in 8 splits: 12 chunks per split switch, 24 do not.
     assert hip_lib.describe(3072, 3072, 6144, 768, 8, BF16).startswith("tiled bm256 bn128 waves2x4 ring3 block512 grid2304")
     assert hip_lib.describe(3072, 3072, 12288, 1536, 8, BF16).startswith("tiled bm256 bn256 waves2x2 ring2 block256 grid1152")
-    # F32 on whole rounds (512 workgroups) keeps 256x256 tiles.
-    assert hip_lib.describe(2048, 4096, 4096, 1024, 4, 0).startswith("tiled bm256 bn256 waves2x2 ring2 block256 grid512")

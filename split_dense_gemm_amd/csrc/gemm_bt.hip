@@ -1174,18 +1174,20 @@ static GemmPlan plan_by_shape(int dtype, int64_t M, int64_t N, int64_t K, int64_
     // 1.049 to 1.011x the faster of the two tiles at geometric mean.  With
     // B as [K,N] the 256x128 kernel was 3-7% slower on four such grids, and
     // 256x256 stays.
-    // F32 with B as [N,K]: the large tiles run at the F32 MFMA rate and are
-    // bound by MFMA time rather than by staging, so the tile that packs the
-    // rounds best wins: the fewest rounds x tile area x a per-tile factor
-    // (256x256 1, 256x128 1.05, 128x128 1.1; ties to the larger tile).  Over
-    // 68 F32 shapes and splits the large-tile rules sent to 256x256 or
-    // 256x128 tiles (M 1024-3072, N 1536-6144, K 2048 and 8192, 1-4 splits),
-    // each timed with all three tiles, this picks the fastest every time:
-    // 0.91x the earlier choice at geometric mean, 0.79x at best
-    // (2048x4608x8192 in one split on 128x128 tiles: 1951 -> 1546 us).
+    // F32: the large tiles run at the F32 MFMA rate and are bound by MFMA
+    // time rather than by staging, so the tile that packs the rounds best
+    // wins: the fewest rounds x tile area x a per-tile factor (256x256 1,
+    // 256x128 1.05, 128x128 1.1; ties to the larger tile; B as [K,N] has no
+    // 128x128 kernel).  Over 68 F32 shapes and splits the large-tile rules
+    // sent to 256x256 or 256x128 tiles (M 1024-3072, N 1536-6144, K 2048 and
+    // 8192, 1-4 splits, B as [N,K]), each timed with all three tiles, this
+    // picks the fastest every time: 0.91x the earlier choice at geometric
+    // mean, 0.79x at best (2048x4608x8192 in one split on 128x128 tiles:
+    // 1951 -> 1546 us).  B as [K,N], 256x128 against 256x256: 0.79-0.89x on
+    // grids of 288-576 256x256 workgroups, 1.04x on a whole round of 512.
     const bool large = M % 256 == 0 && ((N % 256 == 0 && (M / 256) * (N / 256) * splits >= 256) ||
                                         (M / 256) * cdiv(N, 128) * splits >= 256);
-    if (large && dtype == 0 && layout == kLayoutNK) {
+    if (large && dtype == 0) {
         struct Tile { int bm, bn, wm, wn; double factor; };
         const Tile tiles[] = {{256, 256, 2, 2, 1.0}, {256, 128, 2, 4, 1.05}, {128, 128, 2, 2, 1.1}};
         const Tile* best = nullptr;
@@ -1193,6 +1195,7 @@ static GemmPlan plan_by_shape(int dtype, int64_t M, int64_t N, int64_t K, int64_
         double best_cost = 0.0;
         for (const Tile& t : tiles) {
             if (t.bn == 256 && N % 256 != 0) continue;
+            if (t.bm == 128 && layout != kLayoutNK) continue;
             const int64_t wg = (M / t.bm) * cdiv(N, t.bn) * splits;
             const double cost = (double)((wg + 255) / 256) * t.bm * t.bn * t.factor;
             if (!best || cost < best_cost * (1.0 - 1e-9)) { best = &t; best_wg = wg; best_cost = cost; }

@@ -317,7 +317,8 @@ def test_short_last_round_takes_256x128_tiles(hip_lib):
     round of 256x256 workgroups would be at most half full: for 16-bit inputs
     in one or two splits with 257-384 workgroups or with at most 12 chunks
     per split.  F32 takes the tile that packs the rounds best, 128x128
-    included.  Other counts and B as [K,N] keep 256x256 tiles."""
+    included with B as [N,K].  Otherwise 256x256 tiles stay, and always for
+    16-bit inputs with B as [K,N]."""
     half = [(4096, 4608, 4096, 4096, 1), (3072, 6144, 1536, 1536, 1), (2048, 6144, 3072, 1536, 2)]
     full = [(2048, 4096, 4096, 512, 8), (4096, 4096, 8192, 2048, 4), (2048, 7168, 2048, 1024, 2),
             (3072, 6144, 12288, 3072, 4), (768, 3072, 12288, 1536, 8), (4096, 4096, 4096, 4096, 1)]
@@ -332,14 +333,17 @@ def test_short_last_round_takes_256x128_tiles(hip_lib):
         for describe in (hip_lib.describe, hip_lib.describe_bn):
             assert describe(*shape, BF16).startswith(f"tiled bm256 bn256 waves2x2 ring2 block256 grid{wg}")
     # F32: the tile with the fewest rounds x tile area x per-tile factor
-    # (256x256 1, 256x128 1.05, 128x128 1.1) among the three; the same
-    # shapes in BF16 (24 chunks per split) and B as [K,N] keep 256x256 tiles.
-    f32 = [((3072, 3072, 12288, 1536, 8), "bm256 bn128 waves2x4 ring3 block512 grid2304", 1152),
-           ((3072, 3072, 6144, 1536, 4), "bm128 bn128 waves2x2 ring4 block256 grid2304", 576),
-           ((2048, 4096, 4096, 1024, 4), "bm256 bn256 waves2x2 ring2 block256 grid512", 512)]
-    for shape, plan, wg in f32:
-        assert hip_lib.describe(*shape, 0) == f"tiled {plan}", shape
-        assert hip_lib.describe_bn(*shape, 0).startswith(f"tiled bm256 bn256 waves2x2 ring2 block256 grid{wg}")
+    # (256x256 1, 256x128 1.05, 128x128 1.1) among the three (B as [K,N]: no
+    # 128x128); the same shapes in BF16 (24 chunks per split) keep 256x256.
+    f32 = [((3072, 3072, 12288, 1536, 8), "bm256 bn128 waves2x4 ring3 block512 grid2304",
+            "bm256 bn128 waves2x4 ring3 block512 grid2304", 1152),
+           ((3072, 3072, 6144, 1536, 4), "bm128 bn128 waves2x2 ring4 block256 grid2304",
+            "bm256 bn128 waves2x4 ring3 block512 grid1152", 576),
+           ((2048, 4096, 4096, 1024, 4), "bm256 bn256 waves2x2 ring2 block256 grid512",
+            "bm256 bn256 waves2x2 ring2 block256 grid512", 512)]
+    for shape, plan_nk, plan_kn, wg in f32:
+        assert hip_lib.describe(*shape, 0) == f"tiled {plan_nk}", shape
+        assert hip_lib.describe_bn(*shape, 0) == f"tiled {plan_kn}", shape
         assert hip_lib.describe(*shape, BF16).startswith(f"tiled bm256 bn256 waves2x2 ring2 block256 grid{wg}")
     # F32 on 288 256x128 workgroups (144 256x256 ones): 128x128 tiles.
     assert hip_lib.describe(2048, 4608, 8192, 8192, 1, 0) == "tiled bm128 bn128 waves2x2 ring4 block256 grid576"

@@ -37,9 +37,13 @@
  * between calls and is safe to call from several threads.
  *
  * Errors: arguments are checked on the host before anything is enqueued; a
- * non-zero status means nothing was launched.  SPLITK_OK means the kernels
- * were enqueued on `stream`; execution is asynchronous and a device fault
- * would surface at the caller's next synchronisation.  There is no host
+ * non-zero status other than SPLITK_ERR_LAUNCH means nothing was launched.
+ * SPLITK_ERR_LAUNCH means the HIP runtime refused a launch: from a call that
+ * enqueues two kernels (a GEMM and its accumulation pass) it can come after
+ * the GEMM was already enqueued, and the partials then receive the GEMM's
+ * result while C is left as it was.  SPLITK_OK means the kernels were
+ * enqueued on `stream`; execution is asynchronous and a device fault would
+ * surface at the caller's next synchronisation.  There is no host
  * synchronisation, allocation or stream query inside, so the calls may be
  * captured into a HIP graph.  On success every element of partials (and of C)
  * is overwritten; nothing past their ends is touched.
@@ -71,7 +75,9 @@ typedef enum {
     SPLITK_ERR_ALIGN = 6,  /* a base pointer is not 16-byte aligned                 */
     SPLITK_ERR_RANGE = 7,  /* a buffer holds 2^31 elements or more                  */
     SPLITK_ERR_LAUNCH = 8, /* the HIP runtime refused the launch                    */
-    SPLITK_ERR_WORKSPACE = 9 /* workspace smaller than the chosen geometry needs    */
+    SPLITK_ERR_WORKSPACE = 9, /* workspace smaller than the chosen geometry needs   */
+    SPLITK_ERR_PLAN = 10   /* splitk_gemm_planned: the named configuration is not   */
+                           /* instantiated or does not fit the problem              */
 } splitk_status;
 
 /*
@@ -229,6 +235,38 @@ int splitk_describe(int64_t M, int64_t N, int64_t K, int64_t k_per_split, int64_
 /* As splitk_describe, for splitk_gemm_bn (B stored [K,N]). */
 int splitk_describe_bn(int64_t M, int64_t N, int64_t K, int64_t k_per_split, int64_t splits,
                        int dtype, char* buf, int64_t len);
+
+/*
+ * Test and tuning hook: the operation of splitk_gemm_bt (b_layout 0, B
+ * [N,K]) or splitk_gemm_bn (b_layout 1, B [K,N]) with a named kernel
+ * configuration instead of the library's own choice, so that every
+ * instantiated configuration can be run and checked.  The result is the same
+ * operation; only speed differs.  When C is not NULL the accumulation pass
+ * the fused calls run follows on the same stream (C of out_dtype, as in
+ * splitk_gemm_bt_reduce_typed); when it is NULL only the GEMM runs and
+ * out_dtype is ignored.
+ *   plan   NUL-terminated text, one of
+ *            "wavek,BM,BN,WAVES,STAGES"      register-staged skinny kernel
+ *            "wavekdma,BM,BN,WAVES,REGCHUNKS" skinny kernel, last chunk by
+ *                                             LDS DMA (B [N,K] only)
+ *            "tiled,BM,BN,WM,WN[,RING]"       large-tile kernel, RING LDS
+ *                                             buffers (default: the tile's)
+ *          naming an instantiated configuration (the lists in gemm_bt.hip).
+ * Every check of splitk_gemm_bt applies first.  Returns SPLITK_ERR_NULL for a
+ * NULL plan, SPLITK_ERR_PLAN (nothing launched) if the text names no
+ * instantiated configuration for this layout, its row tile BM does not
+ * divide M, or the DMA-tail kernel's waves cannot hold a split's chunks
+ * (more than WAVES x (REGCHUNKS + 1) 128-byte chunks).  Host state: none;
+ * the text is read during the call only.
+ */
+int splitk_gemm_planned(const char* plan, int b_layout, const void* A, const void* B, float* partials,
+                        void* C, int64_t M, int64_t N, int64_t K, int64_t k_per_split, int64_t splits,
+                        int dtype, int out_dtype, void* stream);
+
+/* As splitk_describe, for the configuration `plan` names (statuses as for
+ * splitk_gemm_planned, minus the pointer checks). */
+int splitk_describe_planned(const char* plan, int b_layout, int64_t M, int64_t N, int64_t K,
+                            int64_t k_per_split, int64_t splits, int dtype, char* buf, int64_t len);
 
 #ifdef __cplusplus
 }

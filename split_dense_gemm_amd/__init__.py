@@ -11,11 +11,13 @@ from ._lib import (  # noqa: F401
     choose_splits,
     describe,
     describe_bn,
+    describe_planned,
     gemm_bn,
     gemm_bn_reduce,
     gemm_bt,
     gemm_bt_auto,
     gemm_bt_reduce,
+    gemm_planned,
     header_functions,
     library_built,
     load,

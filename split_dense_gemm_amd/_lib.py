@@ -23,8 +23,10 @@ DTYPE_CODE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 _STATUS_NAMES = {
     0: "SPLITK_OK", 1: "SPLITK_ERR_NULL", 2: "SPLITK_ERR_DTYPE", 3: "SPLITK_ERR_SHAPE",
     4: "SPLITK_ERR_SPLIT", 5: "SPLITK_ERR_ALIAS", 6: "SPLITK_ERR_ALIGN", 7: "SPLITK_ERR_RANGE",
-    8: "SPLITK_ERR_LAUNCH", 9: "SPLITK_ERR_WORKSPACE",
+    8: "SPLITK_ERR_LAUNCH", 9: "SPLITK_ERR_WORKSPACE", 10: "SPLITK_ERR_PLAN",
 }
+
+LAYOUT_CODE = {"nk": 0, "kn": 1}
 
 _lib = None
 
@@ -81,6 +83,11 @@ def load():
     lib.splitk_reduce_for_gemm.restype = I
     lib.splitk_describe.argtypes = [I64, I64, I64, I64, I64, I, ctypes.c_char_p, I64]
     lib.splitk_describe.restype = I
+    lib.splitk_gemm_planned.argtypes = [ctypes.c_char_p, I, P, P, P, P, I64, I64, I64, I64, I64, I, I, P]
+    lib.splitk_gemm_planned.restype = I
+    lib.splitk_describe_planned.argtypes = [ctypes.c_char_p, I, I64, I64, I64, I64, I64, I,
+                                            ctypes.c_char_p, I64]
+    lib.splitk_describe_planned.restype = I
     _lib = lib
     return lib
 
@@ -283,6 +290,29 @@ def describe(M: int, N: int, K: int, k_per_split: int, splits: int, dtype) -> st
     code = _code(dtype)
     buf = ctypes.create_string_buffer(128)
     _check(load().splitk_describe(M, N, K, k_per_split, splits, code, buf, len(buf)))
+    return buf.value.decode()
+
+
+def gemm_planned(plan: str, A: torch.Tensor, B: torch.Tensor, partials: torch.Tensor, k_per_split: int,
+                 splits: int, C=None, layout: str = "nk", stream=None) -> torch.Tensor:
+    """gemm_bt (layout "nk") or gemm_bn (layout "kn") with the kernel
+    configuration `plan` names, followed by the slab sum into C when C is
+    given (see splitk_gemm_planned in splitk.h).  A test and tuning hook."""
+    M, N, K, dt = _operands(A, B) if layout == "nk" else _operands_kn(A, B)
+    _f32_out(partials, "partials", splits * M * N)
+    out = _out(C, M * N) if C is not None else 0
+    _check(load().splitk_gemm_planned(plan.encode(), LAYOUT_CODE[layout], A.data_ptr(), B.data_ptr(),
+                                      partials.data_ptr(), None if C is None else C.data_ptr(), M, N, K,
+                                      int(k_per_split), int(splits), dt, out, _stream(stream)))
+    return partials if C is None else C
+
+
+def describe_planned(plan: str, M: int, N: int, K: int, k_per_split: int, splits: int, dtype,
+                     layout: str = "nk") -> str:
+    """The configuration gemm_planned runs for this plan text and problem."""
+    buf = ctypes.create_string_buffer(128)
+    _check(load().splitk_describe_planned(plan.encode(), LAYOUT_CODE[layout], M, N, K, k_per_split, splits,
+                                          _code(dtype), buf, len(buf)))
     return buf.value.decode()
 
 

@@ -1108,16 +1108,15 @@ bool tiled_config_exists(int layout, int bm, int bn, int wm, int wn, int nbuf) {
     return false;
 }
 
-// Optional override for tuning sweeps and tests: SPLITK_PLAN set to
-// "wavek,BM,BN,WAVES,STAGES" or "tiled,BM,BN,WM,WN" forces that instantiated
-// configuration wherever its tile divides the problem.  Read on every call
-// (a getenv is negligible next to a launch); unset or unknown values leave
-// the automatic choice in place.
-static bool forced_plan(int layout, int* kind, int* v) {
-    const char* e = getenv("SPLITK_PLAN");
+// A named configuration (tests and tuning sweeps, through
+// splitk_gemm_planned): "wavek,BM,BN,WAVES,STAGES", "wavekdma,BM,BN,WAVES,
+// REGCHUNKS" or "tiled,BM,BN,WM,WN[,RING]" (RING: LDS chunk buffers, default
+// the tile's own).  True if the text names an instantiated configuration
+// for this layout of B; *kind and v[0..4] then describe it.
+static bool parse_plan(const char* text, int layout, int* kind, int* v) {
     char name[16] = {0};  // "wavek", "wavekdma" or "tiled"
     v[4] = 0;
-    const int got = e ? sscanf(e, "%15[a-z],%d,%d,%d,%d,%d", name, &v[0], &v[1], &v[2], &v[3], &v[4]) : 0;
+    const int got = text ? sscanf(text, "%15[a-z],%d,%d,%d,%d,%d", name, &v[0], &v[1], &v[2], &v[3], &v[4]) : 0;
     if (got != 5 && got != 6) return false;
     if (!strcmp(name, "wavek") && got == 5 && wavek_config_exists(layout, v[0], v[1], v[2], v[3])) {
         *kind = kWaveK;
@@ -1135,22 +1134,14 @@ static bool forced_plan(int layout, int* kind, int* v) {
     return false;
 }
 
-// The configuration the shape rules pick (or the override forces).
+// The configuration the shape rules pick.
 static GemmPlan plan_by_shape(int dtype, int64_t M, int64_t N, int64_t K, int64_t kps,
                               int64_t splits, int layout) {
     (void)K;
     const int64_t es = dtype == 0 ? 4 : 2;
     const int64_t ck = 128 / es;  // elements per 128-byte chunk
     const int64_t max_chunks = (kps + ck - 1) / ck;  // chunks of the longest split
-    int fk, f[5];
     auto cdiv = [](int64_t a, int64_t b) { return (a + b - 1) / b; };
-    if (forced_plan(layout, &fk, f) && M % f[0] == 0 &&
-        (fk != kWaveKDma || max_chunks <= (int64_t)f[2] * (f[3] + 1))) {
-        const int64_t wg = (M / f[0]) * cdiv(N, f[1]) * splits;
-        if (fk == kTiled)
-            return GemmPlan{kTiled, f[0], f[1], f[2] * f[3], f[2], wg, f[2] * f[3] * 64, layout, f[4]};
-        return GemmPlan{fk, f[0], f[1], f[2], f[3], wg, f[2] * 64, layout};
-    }
     // Large problems: 256x256 tiles (2x2 waves) when there is at least one
     // per CU, else 256x128 tiles on 2x4 waves (two waves per SIMD, measured
     // 5-8% faster than 2x2 for this tile); these read the least L2 data per
@@ -1294,7 +1285,7 @@ GemmPlan plan_gemm(int dtype, int64_t M, int64_t N, int64_t K, int64_t kps, int6
     // can still be faster on fewer CUs: each of its workgroups streams about
     // a third of the bytes per flop.  Take whichever the cost model of the
     // split-count choice rates faster.
-    if (p.kind != kTiled && M % 256 == 0 && getenv("SPLITK_PLAN") == nullptr) {
+    if (p.kind != kTiled && M % 256 == 0) {
         const int64_t tiles = (M / 256) * ((N + 127) / 128) * splits;
         const GemmPlan big{kTiled, 256, 128, 8, 2, tiles, 512, layout, tiled_nbuf(256, 128)};
         if (gemm_cost_us(big, dtype, M, N, K, kps, splits) < gemm_cost_us(p, dtype, M, N, K, kps, splits))
@@ -1302,6 +1293,22 @@ GemmPlan plan_gemm(int dtype, int64_t M, int64_t N, int64_t K, int64_t kps, int6
     }
     p.order = tile_order(p, dtype, M, N, K, kps, splits);
     return p;
+}
+
+bool plan_gemm_named(const char* text, int dtype, int64_t M, int64_t N, int64_t K, int64_t kps,
+                     int64_t splits, int layout, GemmPlan* out) {
+    int kind, f[5];
+    if (!parse_plan(text, layout, &kind, f) || M % f[0] != 0) return false;
+    const int64_t es = dtype == 0 ? 4 : 2;
+    const int64_t max_chunks = (kps * es + 127) / 128;  // chunks of the longest split
+    // The DMA-tail kernel holds at most waves x (register chunks + 1) chunks.
+    if (kind == kWaveKDma && max_chunks > (int64_t)f[2] * (f[3] + 1)) return false;
+    const int64_t wg = (M / f[0]) * ((N + f[1] - 1) / f[1]) * splits;
+    GemmPlan p = kind == kTiled ? GemmPlan{kTiled, f[0], f[1], f[2] * f[3], f[2], wg, f[2] * f[3] * 64, layout, f[4]}
+                                : GemmPlan{kind, f[0], f[1], f[2], f[3], wg, f[2] * 64, layout};
+    p.order = tile_order(p, dtype, M, N, K, kps, splits);
+    *out = p;
+    return true;
 }
 
 hipError_t launch_gemm_bt(const GemmPlan& plan, const void* A, const void* B, float* partials,

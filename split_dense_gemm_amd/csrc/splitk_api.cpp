@@ -100,16 +100,31 @@ int64_t auto_workspace(int64_t splits, int64_t M, int64_t N, int out_dtype) {
     return (splits == 1 && out_dtype == SPLITK_F32) ? 0 : splits * M * N;
 }
 
-// GEMM (and, when C is given, the accumulation pass) for either layout of B.
+// The library's kernel choice for a checked geometry, or the configuration
+// `named` names (NULL: the library's choice).  False if the name is unknown
+// or does not fit the problem.
+bool pick_plan(const char* named, int layout, int dtype, int64_t M, int64_t N, int64_t K, int64_t kps,
+               int64_t splits, splitk::GemmPlan* plan) {
+    if (!named) {
+        *plan = splitk::plan_gemm(dtype, M, N, K, kps, splits, layout);
+        return true;
+    }
+    return splitk::plan_gemm_named(named, dtype, M, N, K, kps, splits, layout, plan);
+}
+
+// GEMM (and, when C is given, the accumulation pass) for either layout of B,
+// with the library's kernel choice or a named one.
 int gemm_entry(int layout, const void* A, const void* B, float* P, void* C, int64_t M, int64_t N,
-               int64_t K, int64_t kps, int64_t splits, int dtype, int out_dtype, void* stream) {
+               int64_t K, int64_t kps, int64_t splits, int dtype, int out_dtype, void* stream,
+               const char* named = nullptr) {
     if (!A || !B || !P) return SPLITK_ERR_NULL;
     int st = check_gemm_shape(M, N, K, kps, splits, dtype, layout);
     if (st != SPLITK_OK) return st;
     if (C && !valid_dtype(out_dtype)) return SPLITK_ERR_DTYPE;
     st = check_gemm_pointers(A, B, P, C, M, N, K, splits, dtype, C ? element_bytes(out_dtype) : 0);
     if (st != SPLITK_OK) return st;
-    const splitk::GemmPlan plan = splitk::plan_gemm(dtype, M, N, K, kps, splits, layout);
+    splitk::GemmPlan plan;
+    if (!pick_plan(named, layout, dtype, M, N, K, kps, splits, &plan)) return SPLITK_ERR_PLAN;
     hipError_t e = splitk::launch_gemm_bt(plan, A, B, P, M, N, K, kps, splits, dtype, (hipStream_t)stream);
     if (e != hipSuccess) return SPLITK_ERR_LAUNCH;
     if (C) e = splitk::launch_slab_reduce_after(plan, P, C, splits, M, N, out_dtype, (hipStream_t)stream);
@@ -117,10 +132,11 @@ int gemm_entry(int layout, const void* A, const void* B, float* P, void* C, int6
 }
 
 int describe_plan(int layout, int64_t M, int64_t N, int64_t K, int64_t k_per_split, int64_t splits,
-                  int dtype, char* buf, int64_t len) {
+                  int dtype, char* buf, int64_t len, const char* named = nullptr) {
     int st = check_gemm_shape(M, N, K, k_per_split, splits, dtype, layout);
     if (st != SPLITK_OK) return st;
-    const splitk::GemmPlan p = splitk::plan_gemm(dtype, M, N, K, k_per_split, splits, layout);
+    splitk::GemmPlan p;
+    if (!pick_plan(named, layout, dtype, M, N, K, k_per_split, splits, &p)) return SPLITK_ERR_PLAN;
     if (buf && len > 0) {
         if (p.kind == splitk::kTiled)
             snprintf(buf, (size_t)len, "tiled bm%d bn%d waves%dx%d ring%d block%d grid%lld%s", p.bm, p.bn,
@@ -154,6 +170,9 @@ const char* splitk_status_str(int status) {
         case SPLITK_ERR_LAUNCH: return "kernel launch failed";
         case SPLITK_ERR_WORKSPACE:
             return "workspace smaller than the chosen split geometry needs (see splitk_choose_splits)";
+        case SPLITK_ERR_PLAN:
+            return "the named kernel configuration is not instantiated for this layout of B or does not "
+                   "fit the problem";
         default: return "unknown status";
     }
 }
@@ -266,6 +285,22 @@ int splitk_gemm_bn_reduce(const void* A, const void* B, float* partials, void* C
 int splitk_describe_bn(int64_t M, int64_t N, int64_t K, int64_t k_per_split, int64_t splits,
                        int dtype, char* buf, int64_t len) {
     return describe_plan(splitk::kLayoutKN, M, N, K, k_per_split, splits, dtype, buf, len);
+}
+
+int splitk_gemm_planned(const char* plan, int b_layout, const void* A, const void* B, float* partials,
+                        void* C, int64_t M, int64_t N, int64_t K, int64_t k_per_split, int64_t splits,
+                        int dtype, int out_dtype, void* stream) {
+    if (!plan) return SPLITK_ERR_NULL;
+    if (b_layout != splitk::kLayoutNK && b_layout != splitk::kLayoutKN) return SPLITK_ERR_PLAN;
+    return gemm_entry(b_layout, A, B, partials, C, M, N, K, k_per_split, splits, dtype,
+                      C ? out_dtype : SPLITK_F32, stream, plan);
+}
+
+int splitk_describe_planned(const char* plan, int b_layout, int64_t M, int64_t N, int64_t K,
+                            int64_t k_per_split, int64_t splits, int dtype, char* buf, int64_t len) {
+    if (!plan) return SPLITK_ERR_NULL;
+    if (b_layout != splitk::kLayoutNK && b_layout != splitk::kLayoutKN) return SPLITK_ERR_PLAN;
+    return describe_plan(b_layout, M, N, K, k_per_split, splits, dtype, buf, len, plan);
 }
 
 }  // extern "C"

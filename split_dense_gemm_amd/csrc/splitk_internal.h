@@ -92,6 +92,13 @@ inline bool stream_slabs(int64_t splits, int64_t M, int64_t N) {
 GemmPlan plan_gemm(int dtype, int64_t M, int64_t N, int64_t K, int64_t kps, int64_t splits,
                    int layout = kLayoutNK);
 
+// The instantiated configuration a plan text names (see splitk_gemm_planned
+// in splitk.h), with the tile order plan_gemm would give it; false if the
+// text names none for this layout of B, its row tile does not divide M, or
+// (DMA-tail kernel) a split holds more chunks than its waves can take.
+bool plan_gemm_named(const char* text, int dtype, int64_t M, int64_t N, int64_t K, int64_t kps,
+                     int64_t splits, int layout, GemmPlan* out);
+
 hipError_t launch_gemm_bt(const GemmPlan& plan, const void* A, const void* B, float* partials,
                           int64_t M, int64_t N, int64_t K, int64_t kps, int64_t splits, int dtype,
                           hipStream_t stream);

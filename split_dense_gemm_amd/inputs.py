@@ -59,20 +59,44 @@ class Workload:
         return [min(self.K, (s + 1) * self.kps) - s * self.kps for s in range(self.splits)]
 
 
-# The measured and tested workloads, named by what they are.
-WORKLOADS = {
-    w.name: w
-    for w in (
-        Workload("f32_m32_n64_k64_s2", "f32", 32, 64, 64, 32, 2, seed=1234,
-                 zero_first_row=True, scale_last_row=True),
-        Workload("bf16_m96_n512_k2048_s4", "bf16", 96, 512, 2048, 512, 4, seed=1235),
-        Workload("bf16_m256_n1024_k2048_s2", "bf16", 256, 1024, 2048, 1024, 2, seed=1236,
-                 zero_first_row=True, scale_last_row=True),
-        Workload("f16_m32_n512_k2080_s4", "f16", 32, 512, 2080, 544, 4, seed=1237),
-        Workload("bf16_m2048_n4096_k4096_s8", "bf16", 2048, 4096, 4096, 512, 8, dist="normal",
-                 seed=1238),
-    )
-}
+# The five measured and tested configurations, named by what they are: the
+# smallest case, the two shapes the first page's headline names, a skinny
+# F16 case whose last split is short, and a large case.
+CONFIGS = (
+    Workload("f32_m32_n64_k64_s2", "f32", 32, 64, 64, 32, 2, seed=1234,
+             zero_first_row=True, scale_last_row=True),
+    Workload("bf16_m96_n512_k2048_s4", "bf16", 96, 512, 2048, 512, 4, seed=1235),
+    Workload("bf16_m256_n1024_k2048_s2", "bf16", 256, 1024, 2048, 1024, 2, seed=1236,
+             zero_first_row=True, scale_last_row=True),
+    Workload("f16_m32_n512_k2080_s4", "f16", 32, 512, 2080, 544, 4, seed=1237),
+    Workload("bf16_m2048_n4096_k4096_s8", "bf16", 2048, 4096, 4096, 512, 8, dist="normal",
+             seed=1238),
+)
+
+# The other (dtype, shape, split) rows the pages time, with seeded uniform
+# [-1,1] inputs: "Aligned shared rows for pipelined NAX on CUDA", table of
+# the section "Measurement protocol" (256x512x2048 at 2 splits in BF16 and
+# F16, 96x512x2048 at 4 splits in F16 and F32, 96x512x512 at 4 splits,
+# 32x64x32 at 1 split), and "Wider consecutive-weight NAX GEMM", table of
+# the section "Performance method" (256x512x2048 at 4 splits in BF16, F16
+# and F32, 128x512x2048 at 8 splits, 96x512x2048 at 8 splits) and its
+# skinny 32-row case at 4 splits.
+PAGE_SHAPES = (
+    Workload("bf16_m256_n512_k2048_s2", "bf16", 256, 512, 2048, 1024, 2, seed=1239),
+    Workload("f16_m256_n512_k2048_s2", "f16", 256, 512, 2048, 1024, 2, seed=1240),
+    Workload("f16_m96_n512_k2048_s4", "f16", 96, 512, 2048, 512, 4, seed=1241),
+    Workload("f32_m96_n512_k2048_s4", "f32", 96, 512, 2048, 512, 4, seed=1242),
+    Workload("bf16_m96_n512_k512_s4", "bf16", 96, 512, 512, 128, 4, seed=1243),
+    Workload("bf16_m32_n64_k32_s1", "bf16", 32, 64, 32, 32, 1, seed=1244),
+    Workload("bf16_m256_n512_k2048_s4", "bf16", 256, 512, 2048, 512, 4, seed=1245),
+    Workload("f16_m256_n512_k2048_s4", "f16", 256, 512, 2048, 512, 4, seed=1246),
+    Workload("f32_m256_n512_k2048_s4", "f32", 256, 512, 2048, 512, 4, seed=1247),
+    Workload("bf16_m128_n512_k2048_s8", "bf16", 128, 512, 2048, 256, 8, seed=1248),
+    Workload("bf16_m96_n512_k2048_s8", "bf16", 96, 512, 2048, 256, 8, seed=1249),
+    Workload("bf16_m32_n512_k2048_s4", "bf16", 32, 512, 2048, 512, 4, seed=1250),
+)
+
+WORKLOADS = {w.name: w for w in CONFIGS + PAGE_SHAPES}
 
 HEADLINE = "bf16_m256_n1024_k2048_s2"
 

@@ -1,3 +1,4 @@
+import functools
 import os
 import sys
 
@@ -44,3 +45,24 @@ def hip_lib():
 
         __graft_entry__.build()
     return sdg
+
+
+LARGEST = "bf16_m2048_n4096_k4096_s8"
+
+
+@functools.lru_cache(maxsize=1)
+def largest_reference():
+    """Operands of the 2048x4096x4096, 8-split BF16 workload and its whole
+    binary64 reference, computed once per session and shared by the tests
+    that compare every output of that workload: (a, b, RP, DP, RC, DC) with
+    RP/DP the [8,M,N] partials and their error scales, RC/DC the unsplit
+    product and its scale (about 1.2 GB of host memory)."""
+    from split_dense_gemm_amd import inputs
+
+    w = inputs.WORKLOADS[LARGEST]
+    a, b = inputs.workload_operands(w)
+    a64 = _oracle.decode(inputs.stored_bits(a), w.dtype)
+    b64 = _oracle.decode(inputs.stored_bits(b), w.dtype)
+    RP, DP, _ = _oracle.splitk_partials(a64, b64, w.kps, w.splits)
+    RC, DC, _ = _oracle.gemm_bt(a64, b64)
+    return a, b, RP, DP, RC, DC

@@ -10,14 +10,13 @@ GPU is present, and the GPU tests cover the same statuses with real buffers.
 from __future__ import annotations
 
 import ctypes
-import os
 
 import pytest
 
 from conftest import gpu_available
 from split_dense_gemm_amd import inputs
 
-OK, NULL, DTYPE, SHAPE, SPLIT, ALIAS, ALIGN, RANGE, LAUNCH, WORKSPACE = range(10)
+OK, NULL, DTYPE, SHAPE, SPLIT, ALIAS, ALIGN, RANGE, LAUNCH, WORKSPACE, PLAN = range(11)
 
 BF16 = inputs.DTYPE_CODES["bf16"]
 
@@ -28,7 +27,8 @@ def test_exports_every_declared_symbol(hip_lib):
                           "splitk_reduce_typed", "splitk_gemm_bt_reduce_typed",
                           "splitk_choose_splits", "splitk_gemm_bt_auto",
                           "splitk_gemm_bn", "splitk_gemm_bn_reduce", "splitk_describe_bn",
-                          "splitk_status_str", "splitk_describe", "splitk_reduce_for_gemm"}
+                          "splitk_status_str", "splitk_describe", "splitk_reduce_for_gemm",
+                          "splitk_gemm_planned", "splitk_describe_planned"}
     lib = hip_lib.load()
     for n in names:
         assert hasattr(lib, n), n
@@ -36,8 +36,8 @@ def test_exports_every_declared_symbol(hip_lib):
 
 def test_status_strings(hip_lib):
     lib = hip_lib.load()
-    texts = [lib.splitk_status_str(s).decode() for s in range(10)]
-    assert texts[0] == "ok" and len(set(texts)) == 10 and "unknown status" not in texts
+    texts = [lib.splitk_status_str(s).decode() for s in range(11)]
+    assert texts[0] == "ok" and len(set(texts)) == 11 and "unknown status" not in texts
     assert lib.splitk_status_str(99).decode() == "unknown status"
 
 
@@ -264,14 +264,12 @@ def test_large_tile_order_choice(hip_lib):
     """256-row tiles take the split-fastest order only on a grid of one round
     (at most 256 workgroups on 256 CUs) with at most 32 MiB of slabs and at
     most 12 chunks of 128 bytes per split, for both B layouts."""
-    tiled = "SPLITK_PLAN"
     fast = [(768, 1536, 1536, 384, 4), (512, 1536, 1536, 192, 8), (2048, 2048, 1024, 512, 2),
             (768, 3072, 1536, 768, 2)]
     major = [(768, 768, 12288, 1536, 8),    # 24 chunks per split
              (1536, 1536, 3072, 768, 4),    # 288 workgroups
              (2048, 4096, 1024, 512, 2),    # 64 MiB of slabs
              (768, 1536, 1536, 96, 16)]     # more than eight splits
-    assert tiled not in os.environ
     for describe in (hip_lib.describe, hip_lib.describe_bn):
         for shape in fast:
             text = describe(*shape, BF16)
@@ -350,3 +348,61 @@ def test_short_last_round_takes_256x128_tiles(hip_lib):
     # 16-bit, 1152 workgroups in 8 splits: 12 chunks per split switch, 24 do not.
     assert hip_lib.describe(3072, 3072, 6144, 768, 8, BF16).startswith("tiled bm256 bn128 waves2x4 ring3 block512 grid2304")
     assert hip_lib.describe(3072, 3072, 12288, 1536, 8, BF16).startswith("tiled bm256 bn256 waves2x2 ring2 block256 grid1152")
+
+
+# Named configurations (splitk_describe_planned / splitk_gemm_planned): text
+# that names no instantiated configuration, a row tile that does not divide
+# M, a DMA-tail kernel whose waves cannot hold a split, or an unknown layout
+# are refused with SPLITK_ERR_PLAN; the shape checks come first.
+PLAN_CASES = [
+    ("wavek,32,64,8,2", 0, (256, 1024, 2048, 1024, 2, BF16), OK),
+    ("tiled,256,128,2,4", 0, (512, 1024, 2048, 1024, 2, BF16), OK),
+    ("tiled,256,128,2,4,3", 1, (512, 1024, 2048, 1024, 2, BF16), OK),
+    ("wavekdma,32,64,8,1", 0, (256, 1024, 2048, 1024, 2, BF16), OK),
+    ("wavekdma,32,64,8,1", 0, (256, 1024, 4096, 2048, 2, BF16), PLAN),   # 32 chunks > 8 x 2
+    ("wavekdma,32,64,8,1", 1, (256, 1024, 2048, 1024, 2, BF16), PLAN),   # no [K,N] form
+    ("tiled,256,256,2,2", 0, (128, 1024, 2048, 1024, 2, BF16), PLAN),    # 256 does not divide M
+    ("wavek,32,64,8,3", 0, (256, 1024, 2048, 1024, 2, BF16), PLAN),      # not instantiated
+    ("tiled,128,128,2,2", 1, (256, 1024, 2048, 1024, 2, BF16), PLAN),    # not for [K,N]
+    ("tiled,256,256,2,2,5", 0, (512, 1024, 2048, 1024, 2, BF16), PLAN),  # ring depth not built
+    ("wavek", 0, (256, 1024, 2048, 1024, 2, BF16), PLAN),
+    ("", 0, (256, 1024, 2048, 1024, 2, BF16), PLAN),
+    ("wavek,32,64,8,2", 2, (256, 1024, 2048, 1024, 2, BF16), PLAN),      # unknown layout
+    ("wavek,32,64,8,2", 0, (48, 1024, 2048, 1024, 2, BF16), SHAPE),      # shape checks first
+    ("wavek,32,64,8,2", 0, (256, 1024, 2048, 1024, 3, BF16), SPLIT),
+]
+
+
+@pytest.mark.parametrize("plan,layout,args,status", PLAN_CASES)
+def test_describe_planned_statuses(hip_lib, plan, layout, args, status):
+    buf = ctypes.create_string_buffer(128)
+    got = hip_lib.load().splitk_describe_planned(plan.encode(), layout, *args, buf, len(buf))
+    assert got == status, (plan, layout, args, buf.value)
+    if status == OK:
+        assert buf.value.decode().startswith(plan.split(",")[0] + " "), buf.value
+
+
+def test_describe_planned_null_plan(hip_lib):
+    buf = ctypes.create_string_buffer(128)
+    assert hip_lib.load().splitk_describe_planned(None, 0, 256, 1024, 2048, 1024, 2, BF16, buf,
+                                                  len(buf)) == NULL
+
+
+def test_named_plan_keeps_the_tile_order_rule(hip_lib):
+    """A named configuration takes the tile order the library would give it."""
+    text = hip_lib.describe_planned("wavek,32,64,8,2", 256, 1024, 2048, 1024, 2, BF16)
+    assert text.endswith(" splitfast"), text
+    text = hip_lib.describe_planned("wavek,32,64,8,2", 256, 1024, 2048, 128, 16, BF16)
+    assert "splitfast" not in text, text
+
+
+@pytest.mark.skipif(gpu_available(), reason="made-up pointers are only safe without a GPU")
+def test_gemm_planned_statuses_without_gpu(hip_lib):
+    lib = hip_lib.load()
+    A, B, P, C = 1 << 32, 2 << 32, 3 << 32, 4 << 32
+    args = (256, 1024, 2048, 1024, 2, BF16, 0, None)
+    assert lib.splitk_gemm_planned(None, 0, A, B, P, C, *args) == NULL
+    assert lib.splitk_gemm_planned(b"wavek,32,64,8,3", 0, A, B, P, C, *args) == PLAN
+    assert lib.splitk_gemm_planned(b"wavek,32,64,8,2", 0, A + 4, B, P, C, *args) == ALIGN
+    assert lib.splitk_gemm_planned(b"wavek,32,64,8,2", 0, A, B, A, C, *args) == ALIAS
+    assert lib.splitk_gemm_planned(b"wavek,32,64,8,2", 0, None, B, P, C, *args) == NULL

@@ -17,6 +17,7 @@ import pytest
 import torch
 
 import oracle
+from conftest import LARGEST, largest_reference
 from split_dense_gemm_amd import inputs
 
 pytestmark = pytest.mark.gpu
@@ -143,20 +144,16 @@ def test_auto_direct_path_ignores_a_workspace(sdg):
     assert oracle.normalized_error(oracle.decode(bits, "f32"), RC, DC)[0] <= FINAL_TOL["bf16"]
 
 
-def test_auto_largest_workload_sampled(sdg):
-    """The 2048x4096x4096 BF16 problem through the automatic path: 4096
-    sampled outputs against the reference one by one; no NaN poison left."""
-    w = inputs.WORKLOADS["bf16_m2048_n4096_k4096_s8"]
-    a, b = inputs.workload_operands(w)
-    bits, _ = _auto(sdg, a, b, "f32")
+def test_auto_largest_workload_full(sdg):
+    """The 2048x4096x4096 BF16 problem through the automatic path: every
+    element of C against the binary64 reference; no NaN poison left."""
+    w = inputs.WORKLOADS[LARGEST]
+    a, b, _, _, RC, DC = largest_reference()
+    bits, (kps, S, need) = _auto(sdg, a, b, "f32")
     got = oracle.decode(bits, "f32")
     assert not np.isnan(got).any()
-    rng = np.random.default_rng(12)
-    rows = np.concatenate([rng.integers(0, w.M, 4092), [0, w.M - 1, 0, w.M - 1]])
-    cols = np.concatenate([rng.integers(0, w.N, 4092), [0, w.N - 1, w.N - 1, 0]])
-    _, _, SC, SDC = oracle.sampled(_vals(a), _vals(b), w.kps, w.splits, rows, cols)
-    err, _ = oracle.normalized_error(got[rows, cols], SC, SDC)
-    print(f"  sampled final err {err:.3e}", flush=True)
+    err, _ = oracle.normalized_error(got, RC, DC)
+    print(f"  {w.name} auto S={S} kps={kps}: final err {err:.3e}", flush=True)
     assert err <= FINAL_TOL["bf16"]
 
 

@@ -15,6 +15,7 @@ import pytest
 import torch
 
 import oracle
+from conftest import LARGEST, largest_reference
 from split_dense_gemm_amd import inputs
 
 pytestmark = pytest.mark.gpu
@@ -139,17 +140,20 @@ def test_bn_workloads(sdg, name, poison):
     assert oracle.normalized_error(oracle.decode(cbits, "f32"), RC, DC)[0] <= FINAL_TOL[w.dtype]
 
 
-def test_bn_largest_workload_sampled(sdg):
-    w = inputs.WORKLOADS["bf16_m2048_n4096_k4096_s8"]
-    a, b = inputs.workload_operands(w)
-    P, cbits = run_bn(sdg, a, b, w.kps, w.splits)
-    C = oracle.decode(cbits, "f32")
-    assert not np.isnan(P).any() and not np.isnan(C).any()
-    rng = np.random.default_rng(13)
-    rows = np.concatenate([rng.integers(0, w.M, 4092), [0, w.M - 1, 0, w.M - 1]])
-    cols = np.concatenate([rng.integers(0, w.N, 4092), [0, w.N - 1, w.N - 1, 0]])
-    SP, SDP, SC, SDC = oracle.sampled(_vals(a), _vals(b), w.kps, w.splits, rows, cols)
-    ep, _ = oracle.normalized_error(P[:, rows, cols].T, SP, SDP)
-    ec, _ = oracle.normalized_error(C[rows, cols], SC, SDC)
-    print(f"  sampled partial err {ep:.3e}, final err {ec:.3e}", flush=True)
-    assert ep <= PARTIAL_TOL and ec <= FINAL_TOL["bf16"]
+@pytest.mark.parametrize("poison", ["seven", "nan"])
+def test_bn_largest_workload_full_parity(sdg, poison):
+    """2048x4096x4096 in 8 splits with B stored [K,N] (its own large-tile
+    kernel, streaming slab stores): every partial and every element of C
+    against the binary64 reference, slab by slab, poisoned outputs, guards."""
+    w = inputs.WORKLOADS[LARGEST]
+    print(f"case {w.name} [K,N] poison={poison}", flush=True)
+    a, b, RP, DP, RC, DC = largest_reference()
+    P, cbits = run_bn(sdg, a, b, w.kps, w.splits, poison=poison)
+    worst = 0.0
+    for s in range(w.splits):
+        ep, _ = oracle.normalized_error(P[s], RP[s], DP[s])
+        worst = max(worst, ep)
+        assert ep <= PARTIAL_TOL, f"slab {s}: partial error {ep}"
+    ec, _ = oracle.normalized_error(oracle.decode(cbits, "f32"), RC, DC)
+    print(f"  partial err {worst:.3e}, final err {ec:.3e}", flush=True)
+    assert ec <= FINAL_TOL["bf16"]

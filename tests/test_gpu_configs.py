@@ -1,7 +1,7 @@
 """Every instantiated GEMM kernel configuration against the binary64 reference.
 
-The automatic plan picks one configuration per shape; these tests force each
-instantiated one (through the SPLITK_PLAN override) on a small problem that
+The automatic plan picks one configuration per shape; these tests run each
+instantiated one (named through splitk_gemm_planned) on a small problem that
 spans several tiles, several chunks per wave, a steady-state pipeline pass
 and a short final split whose last chunk is half empty for 16-bit inputs.
 Acceptance as in test_gpu_parity.py (tolerances of "Aligned shared rows for
@@ -69,7 +69,7 @@ CASES = ([("nk", "wavek", c) for c in WAVEK] + [("nk", "wavekdma", c) for c in W
 
 
 def _plan_text(kind, cfg):
-    """Override string; tiled configurations also name their ring depth."""
+    """Plan text; tiled configurations also name their ring depth."""
     return f"{kind}," + ",".join(str(v) for v in cfg)
 
 
@@ -78,24 +78,11 @@ def _case_id(case):
     return f"{layout}:{_plan_text(kind, cfg)}"
 
 
-@pytest.fixture
-def forced(request):
-    layout, kind, cfg = request.param
-    old = os.environ.get("SPLITK_PLAN")
-    os.environ["SPLITK_PLAN"] = _plan_text(kind, cfg)
-    yield layout, kind, cfg
-    if old is None:
-        os.environ.pop("SPLITK_PLAN", None)
-    else:
-        os.environ["SPLITK_PLAN"] = old
-
-
-@pytest.mark.parametrize("forced", CASES, indirect=True, ids=_case_id)
-def test_override_is_honoured(hip_lib, forced):
-    layout, kind, cfg = forced
+@pytest.mark.parametrize("case", CASES, ids=_case_id)
+def test_named_plan_is_honoured(hip_lib, case):
+    layout, kind, cfg = case
     M, N, K, kps, S = _shape(kind, cfg)
-    describe = hip_lib.describe if layout == "nk" else hip_lib.describe_bn
-    text = describe(M, N, K, kps, S, 2)
+    text = hip_lib.describe_planned(_plan_text(kind, cfg), M, N, K, kps, S, 2, layout=layout)
     assert text.startswith(kind) and f"bm{cfg[0]} bn{cfg[1]}" in text, text
     if kind == "tiled":
         assert f"waves{cfg[2]}x{cfg[3]} ring{cfg[4]}" in text, text
@@ -104,15 +91,14 @@ def test_override_is_honoured(hip_lib, forced):
 @pytest.mark.gpu
 @pytest.mark.skipif(not gpu_available(), reason="no GPU")
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
-@pytest.mark.parametrize("forced", CASES, indirect=True, ids=_case_id)
-def test_config_parity(hip_lib, forced, dtype):
-    layout, kind, cfg = forced
+@pytest.mark.parametrize("case", CASES, ids=_case_id)
+def test_config_parity(hip_lib, case, dtype):
+    layout, kind, cfg = case
+    plan = _plan_text(kind, cfg)
     M, N, K, kps, S = _shape(kind, cfg)
-    print(f"case {layout}:{_plan_text(kind, cfg)} {dtype} M{M} N{N} K{K} kps{kps} S{S}", flush=True)
+    print(f"case {layout}:{plan} {dtype} M{M} N{N} K{K} kps{kps} S{S}", flush=True)
     # B as the library receives it: [N,K], or its transpose stored [K,N].
     stored = (lambda t: t) if layout == "nk" else (lambda t: t.T.contiguous())
-    gemm_reduce = hip_lib.gemm_bt_reduce if layout == "nk" else hip_lib.gemm_bn_reduce
-    gemm = hip_lib.gemm_bt if layout == "nk" else hip_lib.gemm_bn
     dev = torch.device("cuda:0")
     a, b = inputs.make_operands(M, N, K, dtype, seed=sum(cfg[:4]),
                                 zero_first_row=True, scale_last_row=True)
@@ -122,8 +108,8 @@ def test_config_parity(hip_lib, forced, dtype):
     RC, DC, _ = oracle.gemm_bt(a64, b64)
     pbuf = inputs.guarded_buffer(S * M * N, "nan").to(dev)
     cbuf = inputs.guarded_buffer(M * N, "nan").to(dev)
-    gemm_reduce(a.to(dev), stored(b).to(dev), pbuf[: S * M * N].view(S, M, N),
-                cbuf[: M * N].view(M, N), kps, S)
+    hip_lib.gemm_planned(plan, a.to(dev), stored(b).to(dev), pbuf[: S * M * N].view(S, M, N), kps, S,
+                         C=cbuf[: M * N].view(M, N), layout=layout)
     torch.cuda.synchronize()
     p, c = pbuf.cpu().numpy(), cbuf.cpu().numpy()
     guard = np.float32(inputs.GUARD_VALUE).view(np.uint32)
@@ -140,7 +126,7 @@ def test_config_parity(hip_lib, forced, dtype):
     eb64 = oracle.decode(inputs.stored_bits(eb), dtype)
     EP, _, _ = oracle.splitk_partials(ea64, eb64, kps, S)
     P = torch.empty(S, M, N, device=dev)
-    gemm(ea.to(dev), stored(eb).to(dev), P, kps, S)
+    hip_lib.gemm_planned(plan, ea.to(dev), stored(eb).to(dev), P, kps, S, layout=layout)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(P.cpu().numpy().astype(np.float64), EP)
 
@@ -164,32 +150,23 @@ def test_tiled_multi_round_exact(hip_lib, case):
     bm, bn = cfg[0], cfg[1]
     M, N, S, kps = 6 * bm, 5 * bn + 40, 8, 96
     K = (S - 1) * kps + 64
-    old = os.environ.get("SPLITK_PLAN")
-    os.environ["SPLITK_PLAN"] = _plan_text("tiled", cfg)
-    try:
-        describe = hip_lib.describe if layout == "nk" else hip_lib.describe_bn
-        text = describe(M, N, K, kps, S, inputs.DTYPES[dtype])
-        print(f"case {layout} {dtype} M{M} N{N} K{K} kps{kps} S{S}: {text}", flush=True)
-        assert f"bm{bm} bn{bn}" in text and "grid288" in text, text
-        stored = (lambda t: t) if layout == "nk" else (lambda t: t.T.contiguous())
-        gemm_reduce = hip_lib.gemm_bt_reduce if layout == "nk" else hip_lib.gemm_bn_reduce
-        dev = torch.device("cuda:0")
-        ea, eb = inputs.exact_operands(M, N, K, dtype, seed=bm + bn + S)
-        ea64 = oracle.decode(inputs.stored_bits(ea), dtype)
-        eb64 = oracle.decode(inputs.stored_bits(eb), dtype)
-        EP, _, _ = oracle.splitk_partials(ea64, eb64, kps, S)
-        EC = EP.sum(axis=0)
-        pbuf = inputs.guarded_buffer(S * M * N, "nan").to(dev)
-        cbuf = inputs.guarded_buffer(M * N, "nan").to(dev)
-        gemm_reduce(ea.to(dev), stored(eb).to(dev), pbuf[: S * M * N].view(S, M, N),
-                    cbuf[: M * N].view(M, N), kps, S)
-        torch.cuda.synchronize()
-        p, c = pbuf.cpu().numpy(), cbuf.cpu().numpy()
-    finally:
-        if old is None:
-            os.environ.pop("SPLITK_PLAN", None)
-        else:
-            os.environ["SPLITK_PLAN"] = old
+    plan = _plan_text("tiled", cfg)
+    text = hip_lib.describe_planned(plan, M, N, K, kps, S, inputs.DTYPES[dtype], layout=layout)
+    print(f"case {layout} {dtype} M{M} N{N} K{K} kps{kps} S{S}: {text}", flush=True)
+    assert f"bm{bm} bn{bn}" in text and "grid288" in text, text
+    stored = (lambda t: t) if layout == "nk" else (lambda t: t.T.contiguous())
+    dev = torch.device("cuda:0")
+    ea, eb = inputs.exact_operands(M, N, K, dtype, seed=bm + bn + S)
+    ea64 = oracle.decode(inputs.stored_bits(ea), dtype)
+    eb64 = oracle.decode(inputs.stored_bits(eb), dtype)
+    EP, _, _ = oracle.splitk_partials(ea64, eb64, kps, S)
+    EC = EP.sum(axis=0)
+    pbuf = inputs.guarded_buffer(S * M * N, "nan").to(dev)
+    cbuf = inputs.guarded_buffer(M * N, "nan").to(dev)
+    hip_lib.gemm_planned(plan, ea.to(dev), stored(eb).to(dev), pbuf[: S * M * N].view(S, M, N), kps, S,
+                         C=cbuf[: M * N].view(M, N), layout=layout)
+    torch.cuda.synchronize()
+    p, c = pbuf.cpu().numpy(), cbuf.cpu().numpy()
     guard = np.float32(inputs.GUARD_VALUE).view(np.uint32)
     assert np.all(p[S * M * N:].view(np.uint32) == guard)
     assert np.all(c[M * N:].view(np.uint32) == guard)
@@ -220,32 +197,23 @@ def test_tiled_split_fastest_exact(hip_lib, case):
     M, N, kps = tm * bm, 2 * bn + 40, 96
     K = (S - 1) * kps + 64
     dtype = "bf16"
-    old = os.environ.get("SPLITK_PLAN")
-    os.environ["SPLITK_PLAN"] = _plan_text("tiled", cfg)
-    try:
-        describe = hip_lib.describe if layout == "nk" else hip_lib.describe_bn
-        text = describe(M, N, K, kps, S, inputs.DTYPES[dtype])
-        print(f"case {layout} {dtype}->{out} M{M} N{N} K{K} kps{kps} S{S}: {text}", flush=True)
-        assert f"bm{bm} bn{bn}" in text and text.endswith("splitfast"), text
-        stored = (lambda t: t) if layout == "nk" else (lambda t: t.T.contiguous())
-        gemm_reduce = hip_lib.gemm_bt_reduce if layout == "nk" else hip_lib.gemm_bn_reduce
-        dev = torch.device("cuda:0")
-        ea, eb = inputs.exact_operands(M, N, K, dtype, seed=bm + bn + S + tm)
-        ea64 = oracle.decode(inputs.stored_bits(ea), dtype)
-        eb64 = oracle.decode(inputs.stored_bits(eb), dtype)
-        EP, _, _ = oracle.splitk_partials(ea64, eb64, kps, S)
-        EC = oracle.encode(EP.sum(axis=0), out).ravel()
-        pbuf = inputs.guarded_buffer(S * M * N, "nan").to(dev)
-        cbuf = inputs.guarded_buffer(M * N, "nan", dtype=out).to(dev)
-        gemm_reduce(ea.to(dev), stored(eb).to(dev), pbuf[: S * M * N].view(S, M, N),
-                    cbuf[: M * N].view(M, N), kps, S)
-        torch.cuda.synchronize()
-        p, c = pbuf.cpu().numpy(), inputs.stored_bits(cbuf.cpu())
-    finally:
-        if old is None:
-            os.environ.pop("SPLITK_PLAN", None)
-        else:
-            os.environ["SPLITK_PLAN"] = old
+    plan = _plan_text("tiled", cfg)
+    text = hip_lib.describe_planned(plan, M, N, K, kps, S, inputs.DTYPES[dtype], layout=layout)
+    print(f"case {layout} {dtype}->{out} M{M} N{N} K{K} kps{kps} S{S}: {text}", flush=True)
+    assert f"bm{bm} bn{bn}" in text and text.endswith("splitfast"), text
+    stored = (lambda t: t) if layout == "nk" else (lambda t: t.T.contiguous())
+    dev = torch.device("cuda:0")
+    ea, eb = inputs.exact_operands(M, N, K, dtype, seed=bm + bn + S + tm)
+    ea64 = oracle.decode(inputs.stored_bits(ea), dtype)
+    eb64 = oracle.decode(inputs.stored_bits(eb), dtype)
+    EP, _, _ = oracle.splitk_partials(ea64, eb64, kps, S)
+    EC = oracle.encode(EP.sum(axis=0), out).ravel()
+    pbuf = inputs.guarded_buffer(S * M * N, "nan").to(dev)
+    cbuf = inputs.guarded_buffer(M * N, "nan", dtype=out).to(dev)
+    hip_lib.gemm_planned(plan, ea.to(dev), stored(eb).to(dev), pbuf[: S * M * N].view(S, M, N), kps, S,
+                         C=cbuf[: M * N].view(M, N), layout=layout)
+    torch.cuda.synchronize()
+    p, c = pbuf.cpu().numpy(), inputs.stored_bits(cbuf.cpu())
     guard = np.float32(inputs.GUARD_VALUE).view(np.uint32)
     assert np.all(p[S * M * N:].view(np.uint32) == guard)
     np.testing.assert_array_equal(p[: S * M * N].astype(np.float64), EP.reshape(-1))

@@ -11,8 +11,6 @@ would land in the next row and fail the element comparison.
 """
 from __future__ import annotations
 
-import os
-
 import numpy as np
 import pytest
 import torch
@@ -55,16 +53,19 @@ def _vals(t):
     return oracle.decode(inputs.stored_bits(t), inputs.dtype_name(t))
 
 
-def _run(sdg, a, b, kps, S, layout):
+def _run(sdg, a, b, kps, S, layout, plan=None):
     dev = torch.device("cuda:0")
     M, N = a.shape[0], b.shape[0]
     pbuf = inputs.guarded_buffer(S * M * N, "nan").to(dev)
     cbuf = inputs.guarded_buffer(M * N, "nan").to(dev)
     P, C = pbuf[: S * M * N].view(S, M, N), cbuf[: M * N].view(M, N)
-    if layout == "nk":
-        sdg.gemm_bt_reduce(a.to(dev), b.to(dev), P, C, kps, S)
+    bd = b.to(dev) if layout == "nk" else b.T.contiguous().to(dev)
+    if plan:
+        sdg.gemm_planned(plan, a.to(dev), bd, P, kps, S, C=C, layout=layout)
+    elif layout == "nk":
+        sdg.gemm_bt_reduce(a.to(dev), bd, P, C, kps, S)
     else:
-        sdg.gemm_bn_reduce(a.to(dev), b.T.contiguous().to(dev), P, C, kps, S)
+        sdg.gemm_bn_reduce(a.to(dev), bd, P, C, kps, S)
     torch.cuda.synchronize()
     p, c = pbuf.cpu().numpy(), cbuf.cpu().numpy()
     assert np.all(p[S * M * N:].view(np.uint32) == GUARD_BITS), "a partials guard changed"
@@ -72,9 +73,9 @@ def _run(sdg, a, b, kps, S, layout):
     return p[: S * M * N].reshape(S, M, N), c[: M * N].reshape(M, N)
 
 
-def _check(sdg, M, N, K, kps, S, dtype, layout, seed):
+def _check(sdg, M, N, K, kps, S, dtype, layout, seed, plan=None):
     a, b = inputs.make_operands(M, N, K, dtype, seed=seed, zero_first_row=True, scale_last_row=True)
-    P, C = _run(sdg, a, b, kps, S, layout)
+    P, C = _run(sdg, a, b, kps, S, layout, plan)
     a64, b64 = _vals(a), _vals(b)
     RP, DP, _ = oracle.splitk_partials(a64, b64, kps, S)
     RC, DC, _ = oracle.gemm_bt(a64, b64)
@@ -106,19 +107,11 @@ def test_kn_tails(sdg, shape, dtype):
 @pytest.mark.parametrize("plan", ["tiled,256,256,2,2", "tiled,256,128,2,2"])
 def test_tiled_tails_forced(sdg, layout, plan):
     """The large-tile kernels with a narrowed last tile (40 columns)."""
-    old = os.environ.get("SPLITK_PLAN")
-    os.environ["SPLITK_PLAN"] = plan
-    try:
-        M, N, K, kps, S = 256, 296, 1248, 608, 3
-        desc = (sdg.describe if layout == "nk" else sdg.describe_bn)(M, N, K, kps, S, torch.bfloat16)
-        print(f"case {layout} {plan} M{M} N{N}: {desc}", flush=True)
-        assert desc.startswith("tiled bm256 bn" + plan.split(",")[2])
-        _check(sdg, M, N, K, kps, S, "bf16", layout, seed=17)
-    finally:
-        if old is None:
-            os.environ.pop("SPLITK_PLAN", None)
-        else:
-            os.environ["SPLITK_PLAN"] = old
+    M, N, K, kps, S = 256, 296, 1248, 608, 3
+    desc = sdg.describe_planned(plan, M, N, K, kps, S, torch.bfloat16, layout=layout)
+    print(f"case {layout} {plan} M{M} N{N}: {desc}", flush=True)
+    assert desc.startswith("tiled bm256 bn" + plan.split(",")[2])
+    _check(sdg, M, N, K, kps, S, "bf16", layout, seed=17, plan=plan)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])

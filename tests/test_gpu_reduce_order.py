@@ -15,8 +15,6 @@ round of workgroups or 32 MiB of slabs).
 """
 from __future__ import annotations
 
-import os
-
 import numpy as np
 import pytest
 import torch
@@ -55,16 +53,6 @@ def sdg(hip_lib):
     return hip_lib
 
 
-@pytest.fixture
-def plan_env():
-    old = os.environ.get("SPLITK_PLAN")
-    yield
-    if old is None:
-        os.environ.pop("SPLITK_PLAN", None)
-    else:
-        os.environ["SPLITK_PLAN"] = old
-
-
 def _slabs(M, N, S, seed):
     gen = torch.Generator().manual_seed(seed)
     return torch.randn(S, M, N, generator=gen) * 3
@@ -84,18 +72,37 @@ def _run(sdg, fn_name, slabs, M, N, geo, out):
     return inputs.stored_bits(cbuf.cpu())
 
 
+def _run_planned(sdg, plan, M, N, geo, out):
+    """The fused call with a named GEMM configuration; returns C's stored
+    bits (guards included) and the slabs the GEMM wrote."""
+    K, kps, S, dt = geo[2], geo[3], geo[4], geo[5]
+    dev = torch.device("cuda:0")
+    a, b = inputs.make_operands(M, N, K, dt, seed=M + N + S)
+    P = torch.empty(S, M, N, device=dev)
+    cbuf = inputs.guarded_buffer(M * N, "nan", dtype=out).to(dev)
+    sdg.gemm_planned(plan, a.to(dev), b.to(dev), P, kps, S, C=cbuf[: M * N].view(M, N))
+    torch.cuda.synchronize()
+    return inputs.stored_bits(cbuf.cpu()), P.cpu()
+
+
 @pytest.mark.parametrize("out", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("geo", GEOMETRIES, ids=lambda g: "x".join(map(str, g[:5])) + f"-{g[5]}"
                          + ("-forced" if g[6] else "") + ("-tiles" if g[7] else "-flat"))
-def test_tile_order_equals_flat_order(sdg, plan_env, geo, out):
+def test_tile_order_equals_flat_order(sdg, geo, out):
     M, N, K, kps, S, dt, plan, tile_order = geo
     if plan:
-        os.environ["SPLITK_PLAN"] = plan
-    text = sdg.describe(M, N, K, kps, S, inputs.DTYPES[dt])
+        text = sdg.describe_planned(plan, M, N, K, kps, S, inputs.DTYPES[dt])
+    else:
+        text = sdg.describe(M, N, K, kps, S, inputs.DTYPES[dt])
     print(f"reduce order: {geo} out={out} plan={text}", flush=True)
     assert ("splitfast" in text) == tile_order, text
-    slabs = _slabs(M, N, S, seed=M + N + S)
-    got = _run(sdg, "tile", slabs, M, N, geo, out)
+    if plan:
+        # A named configuration: its fused call (the GEMM, then the pass in
+        # that GEMM's tile order) against the flat pass over its own slabs.
+        got, slabs = _run_planned(sdg, plan, M, N, geo, out)
+    else:
+        slabs = _slabs(M, N, S, seed=M + N + S)
+        got = _run(sdg, "tile", slabs, M, N, geo, out)
     flat = _run(sdg, "flat", slabs, M, N, geo, out)
     np.testing.assert_array_equal(got, flat)
     guard = GUARD_BITS if out == "f32" else GUARD16[out]

@@ -76,9 +76,15 @@ typedef enum {
     SPLITK_ERR_RANGE = 7,  /* a buffer holds 2^31 elements or more                  */
     SPLITK_ERR_LAUNCH = 8, /* the HIP runtime refused the launch                    */
     SPLITK_ERR_WORKSPACE = 9, /* workspace smaller than the chosen geometry needs   */
-    SPLITK_ERR_PLAN = 10   /* splitk_gemm_planned: the named configuration is not   */
+    SPLITK_ERR_PLAN = 10,  /* splitk_gemm_planned: the named configuration is not   */
                            /* instantiated or does not fit the problem              */
+    SPLITK_ERR_SCRATCH = 11 /* splitk_gemm_bt_auto_noalloc: the slabs would exceed  */
+                            /* the library's static array                           */
 } splitk_status;
+
+/* F32 elements of the library-owned slab array of splitk_gemm_bt_auto_noalloc
+ * (64 MiB per GPU). */
+#define SPLITK_STATIC_SLAB_FLOATS (16LL << 20)
 
 /*
  * Split-K GEMM into F32 partial slabs (first page, "Contract and
@@ -194,6 +200,30 @@ int splitk_choose_splits(int64_t M, int64_t N, int64_t K, int dtype, int out_dty
 int splitk_gemm_bt_auto(const void* A, const void* B, float* workspace, int64_t workspace_elems,
                         void* C, int64_t M, int64_t N, int64_t K, int dtype, int out_dtype,
                         void* stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the
+ * operation of splitk_gemm_bt_auto, same choice of split count, same kernels
+ * and so the same C bit for bit, but with the F32 slabs in a device array the
+ * library owns instead of a caller workspace.  The array holds
+ * SPLITK_STATIC_SLAB_FLOATS floats (64 MiB); every GPU the library runs on
+ * gets its own copy when the library's code is loaded there and keeps it
+ * until the process ends.  Its address is looked up once per device, on the
+ * first call with that device current (the current device must be the one
+ * `stream` runs on).  The call allocates nothing and frees nothing.
+ *   C   [M,N] of out_dtype, written in full.
+ * Every call on one GPU uses that GPU's one array, so calls that may overlap
+ * on one GPU (other streams, other threads) race on it: serialise them.  The
+ * array keeps the last call's slabs; no call needs it to start at zero.
+ * Returns the statuses of splitk_gemm_bt_auto, and SPLITK_ERR_SCRATCH
+ * (nothing launched) when the chosen geometry needs more than
+ * SPLITK_STATIC_SLAB_FLOATS slab elements (splits*M*N; splitk_choose_splits
+ * reports it as workspace_elems); SPLITK_ERR_LAUNCH if the array's address
+ * cannot be obtained.
+ */
+int splitk_gemm_bt_auto_noalloc(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                                int dtype, int out_dtype, void* stream);
 
 /*
  * The same split-K GEMM with B stored [K,N] instead of [N,K]: row k of B holds

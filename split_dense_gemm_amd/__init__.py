@@ -16,6 +16,7 @@ from ._lib import (  # noqa: F401
     gemm_bn_reduce,
     gemm_bt,
     gemm_bt_auto,
+    gemm_bt_auto_noalloc,
     gemm_bt_reduce,
     gemm_planned,
     header_functions,

@@ -23,7 +23,7 @@ DTYPE_CODE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 _STATUS_NAMES = {
     0: "SPLITK_OK", 1: "SPLITK_ERR_NULL", 2: "SPLITK_ERR_DTYPE", 3: "SPLITK_ERR_SHAPE",
     4: "SPLITK_ERR_SPLIT", 5: "SPLITK_ERR_ALIAS", 6: "SPLITK_ERR_ALIGN", 7: "SPLITK_ERR_RANGE",
-    8: "SPLITK_ERR_LAUNCH", 9: "SPLITK_ERR_WORKSPACE", 10: "SPLITK_ERR_PLAN",
+    8: "SPLITK_ERR_LAUNCH", 9: "SPLITK_ERR_WORKSPACE", 10: "SPLITK_ERR_PLAN", 11: "SPLITK_ERR_SCRATCH",
 }
 
 LAYOUT_CODE = {"nk": 0, "kn": 1}
@@ -88,6 +88,8 @@ def load():
     lib.splitk_describe_planned.argtypes = [ctypes.c_char_p, I, I64, I64, I64, I64, I64, I,
                                             ctypes.c_char_p, I64]
     lib.splitk_describe_planned.restype = I
+    lib.splitk_gemm_bt_auto_noalloc.argtypes = [P, P, P, I64, I64, I64, I, I, P]
+    lib.splitk_gemm_bt_auto_noalloc.restype = I
     _lib = lib
     return lib
 
@@ -252,6 +254,16 @@ def gemm_bt_auto(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, workspace=No
         wp, wn = workspace.data_ptr(), workspace.numel()
     _check(load().splitk_gemm_bt_auto(A.data_ptr(), B.data_ptr(), wp, wn, C.data_ptr(), M, N, K, dt,
                                       out, _stream(stream)))
+    return C
+
+
+def gemm_bt_auto_noalloc(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, stream=None) -> torch.Tensor:
+    """gemm_bt_auto with the slabs in the library's own static device array
+    instead of a workspace (see splitk_gemm_bt_auto_noalloc in splitk.h)."""
+    M, N, K, dt = _operands(A, B)
+    out = _out(C, M * N)
+    _check(load().splitk_gemm_bt_auto_noalloc(A.data_ptr(), B.data_ptr(), C.data_ptr(), M, N, K, dt, out,
+                                              _stream(stream)))
     return C
 
 

@@ -170,6 +170,9 @@ const char* splitk_status_str(int status) {
         case SPLITK_ERR_LAUNCH: return "kernel launch failed";
         case SPLITK_ERR_WORKSPACE:
             return "workspace smaller than the chosen split geometry needs (see splitk_choose_splits)";
+        case SPLITK_ERR_SCRATCH:
+            return "the chosen split geometry needs more slab memory than the library's static array "
+                   "holds (16 Mi F32 elements; use splitk_gemm_bt_auto with a workspace)";
         case SPLITK_ERR_PLAN:
             return "the named kernel configuration is not instantiated for this layout of B or does not "
                    "fit the problem";
@@ -261,6 +264,22 @@ int splitk_gemm_bt_auto(const void* A, const void* B, float* workspace, int64_t 
     if (e != hipSuccess) return SPLITK_ERR_LAUNCH;
     e = splitk::launch_slab_reduce_after(plan, workspace, C, s, M, N, out_dtype, (hipStream_t)stream);
     return e == hipSuccess ? SPLITK_OK : SPLITK_ERR_LAUNCH;
+}
+
+int splitk_gemm_bt_auto_noalloc(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                                int dtype, int out_dtype, void* stream) {
+    if (!A || !B || !C) return SPLITK_ERR_NULL;
+    int64_t kps = 0, s = 0, need = 0;
+    int st = splitk_choose_splits(M, N, K, dtype, out_dtype, &kps, &s, &need);
+    if (st != SPLITK_OK) return st;
+    if (need > splitk::kStaticSlabFloats) return SPLITK_ERR_SCRATCH;
+    if (need == 0) {
+        // One split, F32 output: the GEMM writes C itself, no slab memory.
+        return splitk_gemm_bt_auto(A, B, nullptr, 0, C, M, N, K, dtype, out_dtype, stream);
+    }
+    float* slabs = splitk::static_slabs();
+    if (!slabs) return SPLITK_ERR_LAUNCH;
+    return splitk_gemm_bt_auto(A, B, slabs, splitk::kStaticSlabFloats, C, M, N, K, dtype, out_dtype, stream);
 }
 
 int splitk_describe(int64_t M, int64_t N, int64_t K, int64_t k_per_split, int64_t splits, int dtype,

@@ -88,6 +88,15 @@ inline bool stream_slabs(int64_t splits, int64_t M, int64_t N) {
     return splits > 1 && splits * M * N * 4 > kStreamSlabBytes;
 }
 
+// Capacity of the library-owned slab array (static_slabs.hip): 16 Mi F32
+// elements, 64 MiB per GPU.
+constexpr int64_t kStaticSlabFloats = int64_t(16) << 20;
+
+// Device address of that array on the current device, looked up on the
+// first call per device (hipGetSymbolAddress) and cached; NULL if the
+// lookup fails.
+float* static_slabs();
+
 // Chooses the kernel configuration for a validated problem.
 GemmPlan plan_gemm(int dtype, int64_t M, int64_t N, int64_t K, int64_t kps, int64_t splits,
                    int layout = kLayoutNK);

@@ -16,7 +16,7 @@ import pytest
 from conftest import gpu_available
 from split_dense_gemm_amd import inputs
 
-OK, NULL, DTYPE, SHAPE, SPLIT, ALIAS, ALIGN, RANGE, LAUNCH, WORKSPACE, PLAN = range(11)
+OK, NULL, DTYPE, SHAPE, SPLIT, ALIAS, ALIGN, RANGE, LAUNCH, WORKSPACE, PLAN, SCRATCH = range(12)
 
 BF16 = inputs.DTYPE_CODES["bf16"]
 
@@ -28,7 +28,8 @@ def test_exports_every_declared_symbol(hip_lib):
                           "splitk_choose_splits", "splitk_gemm_bt_auto",
                           "splitk_gemm_bn", "splitk_gemm_bn_reduce", "splitk_describe_bn",
                           "splitk_status_str", "splitk_describe", "splitk_reduce_for_gemm",
-                          "splitk_gemm_planned", "splitk_describe_planned"}
+                          "splitk_gemm_planned", "splitk_describe_planned",
+                          "splitk_gemm_bt_auto_noalloc"}
     lib = hip_lib.load()
     for n in names:
         assert hasattr(lib, n), n
@@ -36,8 +37,8 @@ def test_exports_every_declared_symbol(hip_lib):
 
 def test_status_strings(hip_lib):
     lib = hip_lib.load()
-    texts = [lib.splitk_status_str(s).decode() for s in range(11)]
-    assert texts[0] == "ok" and len(set(texts)) == 11 and "unknown status" not in texts
+    texts = [lib.splitk_status_str(s).decode() for s in range(12)]
+    assert texts[0] == "ok" and len(set(texts)) == 12 and "unknown status" not in texts
     assert lib.splitk_status_str(99).decode() == "unknown status"
 
 

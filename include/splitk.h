@@ -281,12 +281,17 @@ int splitk_describe_bn(int64_t M, int64_t N, int64_t K, int64_t k_per_split, int
  *                                             LDS DMA (B [N,K] only)
  *            "tiled,BM,BN,WM,WN[,RING]"       large-tile kernel, RING LDS
  *                                             buffers (default: the tile's)
+ *            "tiledp,BM,BN,WM,WN"            persistent large-tile kernel:
+ *                                             at most one workgroup per CU,
+ *                                             each walking several tiles
+ *                                             (B [N,K] only)
  *          naming an instantiated configuration (the lists in gemm_bt.hip).
  * Every check of splitk_gemm_bt applies first.  Returns SPLITK_ERR_NULL for a
  * NULL plan, SPLITK_ERR_PLAN (nothing launched) if the text names no
  * instantiated configuration for this layout, its row tile BM does not
- * divide M, or the DMA-tail kernel's waves cannot hold a split's chunks
- * (more than WAVES x (REGCHUNKS + 1) 128-byte chunks).  Host state: none;
+ * divide M, the DMA-tail kernel's waves cannot hold a split's chunks
+ * (more than WAVES x (REGCHUNKS + 1) 128-byte chunks), or a persistent
+ * configuration has fewer than 8 tiles (one per XCD).  Host state: none;
  * the text is read during the call only.
  */
 int splitk_gemm_planned(const char* plan, int b_layout, const void* A, const void* B, float* partials,

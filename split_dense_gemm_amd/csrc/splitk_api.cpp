@@ -139,9 +139,9 @@ int describe_plan(int layout, int64_t M, int64_t N, int64_t K, int64_t k_per_spl
     if (!pick_plan(named, layout, dtype, M, N, K, k_per_split, splits, &p)) return SPLITK_ERR_PLAN;
     if (buf && len > 0) {
         if (p.kind == splitk::kTiled)
-            snprintf(buf, (size_t)len, "tiled bm%d bn%d waves%dx%d ring%d block%d grid%lld%s", p.bm, p.bn,
-                     p.stages, p.waves / p.stages, p.nbuf, p.block, (long long)p.grid,
-                     p.order == 1 ? " splitfast" : "");
+            snprintf(buf, (size_t)len, "tiled bm%d bn%d waves%dx%d ring%d block%d grid%lld%s%s", p.bm, p.bn,
+                     p.stages, p.waves / p.stages, p.nbuf, p.block, (long long)splitk::launch_grid(p),
+                     p.order == 1 ? " splitfast" : "", p.persist ? " persistent" : "");
         else
             snprintf(buf, (size_t)len, "%s bm%d bn%d waves%d stages%d block%d grid%lld%s",
                      p.kind == splitk::kWaveKDma ? "wavekdma" : "wavek", p.bm, p.bn, p.waves, p.stages,

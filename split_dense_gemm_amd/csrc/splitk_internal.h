@@ -33,6 +33,7 @@ struct GemmPlan {
     int layout;    // BLayout of B
     int nbuf = 0;  // tiled kernels: chunk buffers in the LDS ring (0: the tile's default)
     int order = 0; // 1 = splits of a tile on one XCD (skinny_tile; the large-tile kernel's tile order)
+    int persist = 0; // tiled kernels: one workgroup per CU walking several tiles
 };
 
 // Renumbers workgroups so that consecutive logical ids run on one XCD.
@@ -108,6 +109,7 @@ GemmPlan plan_gemm(int dtype, int64_t M, int64_t N, int64_t K, int64_t kps, int6
 bool plan_gemm_named(const char* text, int dtype, int64_t M, int64_t N, int64_t K, int64_t kps,
                      int64_t splits, int layout, GemmPlan* out);
 
+int64_t launch_grid(const GemmPlan& p);
 hipError_t launch_gemm_bt(const GemmPlan& plan, const void* A, const void* B, float* partials,
                           int64_t M, int64_t N, int64_t K, int64_t kps, int64_t splits, int dtype,
                           hipStream_t stream);

@@ -329,8 +329,13 @@ def test_short_last_round_takes_256x128_tiles(hip_lib):
     for shape in full:
         wg = (shape[0] // 256) * (shape[1] // 256) * shape[4]
         assert not (256 < wg <= 384 and shape[4] <= 2), shape
-        for describe in (hip_lib.describe, hip_lib.describe_bn):
-            assert describe(*shape, BF16).startswith(f"tiled bm256 bn256 waves2x2 ring2 block256 grid{wg}")
+        # Several rounds of splits of at most 16 chunks run persistently on
+        # 256 workgroups (B as [N,K] only).
+        persistent = wg > 256 and shape[3] * 2 // 128 <= 16
+        assert hip_lib.describe(*shape, BF16) == (
+            "tiled bm256 bn256 waves2x2 ring2 block256 grid256 persistent" if persistent
+            else f"tiled bm256 bn256 waves2x2 ring2 block256 grid{wg}"), shape
+        assert hip_lib.describe_bn(*shape, BF16).startswith(f"tiled bm256 bn256 waves2x2 ring2 block256 grid{wg}")
     # F32: the tile with the fewest rounds x tile area x per-tile factor
     # (256x256 1, 256x128 1.05, 128x128 1.1) among the three (B as [K,N]: no
     # 128x128); the same shapes in BF16 (24 chunks per split) keep 256x256.
@@ -343,12 +348,39 @@ def test_short_last_round_takes_256x128_tiles(hip_lib):
     for shape, plan_nk, plan_kn, wg in f32:
         assert hip_lib.describe(*shape, 0) == f"tiled {plan_nk}", shape
         assert hip_lib.describe_bn(*shape, 0) == f"tiled {plan_kn}", shape
-        assert hip_lib.describe(*shape, BF16).startswith(f"tiled bm256 bn256 waves2x2 ring2 block256 grid{wg}")
+        grid = "grid256 persistent" if shape[3] * 2 // 128 <= 16 else f"grid{wg}"
+        assert hip_lib.describe(*shape, BF16) == f"tiled bm256 bn256 waves2x2 ring2 block256 {grid}", shape
     # F32 on 288 256x128 workgroups (144 256x256 ones): 128x128 tiles.
     assert hip_lib.describe(2048, 4608, 8192, 8192, 1, 0) == "tiled bm128 bn128 waves2x2 ring4 block256 grid576"
     # 16-bit, 1152 workgroups in 8 splits: 12 chunks per split switch, 24 do not.
     assert hip_lib.describe(3072, 3072, 6144, 768, 8, BF16).startswith("tiled bm256 bn128 waves2x4 ring3 block512 grid2304")
     assert hip_lib.describe(3072, 3072, 12288, 1536, 8, BF16).startswith("tiled bm256 bn256 waves2x2 ring2 block256 grid1152")
+
+
+def test_persistent_large_tiles_rule(hip_lib):
+    """256x256 tiles with B as [N,K] run persistently (one workgroup per CU
+    walking several tiles) where there are more tiles than CUs and every
+    split is at most 16 chunks; one round, longer splits, B as [K,N] and the
+    other tiles keep one workgroup per tile."""
+    yes = [((2048, 4096, 4096, 512, 8), BF16), ((2048, 4096, 4096, 512, 8), 1),
+           ((2048, 4096, 4096, 512, 8), 0), ((2048, 4096, 4096, 1024, 4), BF16),
+           ((4096, 4096, 4096, 256, 16), BF16)]
+    no = [((4096, 4096, 8192, 2048, 4), BF16),   # 32 chunks per split
+          ((2048, 4096, 4096, 1024, 4), 0),       # F32: 32 chunks per split
+          ((4096, 4096, 4096, 4096, 1), BF16),    # one round
+          ((256, 1024, 2048, 1024, 2), BF16)]     # skinny
+    for shape, dt in yes:
+        assert hip_lib.describe(*shape, dt).endswith("grid256 persistent"), (shape, dt)
+        assert "persistent" not in hip_lib.describe_bn(*shape, dt), (shape, dt)
+    for shape, dt in no:
+        assert "persistent" not in hip_lib.describe(*shape, dt), (shape, dt)
+    # Named: "tiledp" is the persistent form, "tiled" never is; fewer tiles
+    # than CUs launch one workgroup per tile.
+    assert hip_lib.describe_planned("tiled,256,256,2,2", 2048, 4096, 4096, 512, 8, BF16).endswith("grid1024")
+    assert hip_lib.describe_planned("tiledp,256,256,2,2", 2048, 4096, 4096, 512, 8, BF16).endswith(
+        "grid256 persistent")
+    assert hip_lib.describe_planned("tiledp,256,128,2,4", 512, 1024, 2048, 256, 8, BF16).endswith(
+        "grid128 persistent")
 
 
 # Named configurations (splitk_describe_planned / splitk_gemm_planned): text
@@ -371,6 +403,12 @@ PLAN_CASES = [
     ("wavek,32,64,8,2", 2, (256, 1024, 2048, 1024, 2, BF16), PLAN),      # unknown layout
     ("wavek,32,64,8,2", 0, (48, 1024, 2048, 1024, 2, BF16), SHAPE),      # shape checks first
     ("wavek,32,64,8,2", 0, (256, 1024, 2048, 1024, 3, BF16), SPLIT),
+    ("tiledp,256,256,2,2", 0, (2048, 4096, 4096, 512, 8, BF16), OK),
+    ("tiledp,256,128,2,4", 0, (512, 1024, 2048, 256, 8, BF16), OK),
+    ("tiledp,256,256,2,2", 1, (2048, 4096, 4096, 512, 8, BF16), PLAN),   # no [K,N] form
+    ("tiledp,256,256,2,2,2", 0, (2048, 4096, 4096, 512, 8, BF16), PLAN), # no ring argument
+    ("tiledp,128,128,2,2", 0, (2048, 4096, 4096, 512, 8, BF16), PLAN),   # not instantiated
+    ("tiledp,256,256,2,2", 0, (256, 512, 2048, 1024, 2, BF16), PLAN),    # 4 tiles: an XCD without one
 ]
 
 
@@ -380,7 +418,9 @@ def test_describe_planned_statuses(hip_lib, plan, layout, args, status):
     got = hip_lib.load().splitk_describe_planned(plan.encode(), layout, *args, buf, len(buf))
     assert got == status, (plan, layout, args, buf.value)
     if status == OK:
-        assert buf.value.decode().startswith(plan.split(",")[0] + " "), buf.value
+        kind = plan.split(",")[0]
+        text = buf.value.decode()
+        assert text.startswith(kind.rstrip("p") + " ") and text.endswith(" persistent") == (kind == "tiledp"), text
 
 
 def test_describe_planned_null_plan(hip_lib):

@@ -43,6 +43,7 @@ WAVEKDMA = _configs("SPLITK_WAVEKDMA_CONFIGS")
 TILED = _configs("SPLITK_TILED_CONFIGS")
 KN_WAVEK = _configs("SPLITK_KN_WAVEK_CONFIGS")
 KN_TILED = _configs("SPLITK_KN_TILED_CONFIGS")
+TILED_PT = _configs("SPLITK_TILED_PT_CONFIGS")
 
 
 def _shape(kind, cfg):
@@ -65,7 +66,7 @@ def _shape(kind, cfg):
 
 CASES = ([("nk", "wavek", c) for c in WAVEK] + [("nk", "wavekdma", c) for c in WAVEKDMA] +
          [("nk", "tiled", c) for c in TILED] + [("kn", "wavek", c) for c in KN_WAVEK] +
-         [("kn", "tiled", c) for c in KN_TILED])
+         [("kn", "tiled", c) for c in KN_TILED] + [("nk", "tiledp", c) for c in TILED_PT])
 
 
 def _plan_text(kind, cfg):
@@ -83,9 +84,12 @@ def test_named_plan_is_honoured(hip_lib, case):
     layout, kind, cfg = case
     M, N, K, kps, S = _shape(kind, cfg)
     text = hip_lib.describe_planned(_plan_text(kind, cfg), M, N, K, kps, S, 2, layout=layout)
-    assert text.startswith(kind) and f"bm{cfg[0]} bn{cfg[1]}" in text, text
+    assert text.startswith(kind.rstrip("p")) and f"bm{cfg[0]} bn{cfg[1]}" in text, text
+    assert text.endswith(" persistent") == (kind == "tiledp"), text
     if kind == "tiled":
         assert f"waves{cfg[2]}x{cfg[3]} ring{cfg[4]}" in text, text
+    if kind == "tiledp":
+        assert f"waves{cfg[2]}x{cfg[3]} ring2" in text, text
 
 
 @pytest.mark.gpu
@@ -137,23 +141,29 @@ def test_config_parity(hip_lib, case, dtype):
 # full 16-bit split ends in a half chunk and the last split is short.  With
 # exact-arithmetic inputs every partial and the final sum are exact, so both
 # must match bit for bit (C is the binary64 sum of the exact partials).
-MULTI_ROUND = ([("nk", c, "bf16") for c in TILED] + [("kn", c, "bf16") for c in KN_TILED] +
-               [("nk", TILED[0], "f16"), ("nk", TILED[0], "f32")])
+MULTI_ROUND = ([("nk", "tiled", c, "bf16") for c in TILED] + [("kn", "tiled", c, "bf16") for c in KN_TILED] +
+               [("nk", "tiled", TILED[0], "f16"), ("nk", "tiled", TILED[0], "f32")] +
+               [("nk", "tiledp", c, "bf16") for c in TILED_PT] +
+               [("nk", "tiledp", TILED_PT[0], "f16"), ("nk", "tiledp", TILED_PT[0], "f32")])
 
 
 @pytest.mark.gpu
 @pytest.mark.skipif(not gpu_available(), reason="no GPU")
 @pytest.mark.parametrize("case", MULTI_ROUND,
-                         ids=lambda c: f"{c[0]}:tiled," + ",".join(map(str, c[1])) + f"-{c[2]}")
+                         ids=lambda c: f"{c[0]}:{c[1]}," + ",".join(map(str, c[2])) + f"-{c[3]}")
 def test_tiled_multi_round_exact(hip_lib, case):
-    layout, cfg, dtype = case
+    """On the persistent configurations the 288 tiles run on 256 workgroups:
+    32 of them take a second tile, whose first two chunks are loaded while
+    the first tile's partials are stored."""
+    layout, kind, cfg, dtype = case
     bm, bn = cfg[0], cfg[1]
     M, N, S, kps = 6 * bm, 5 * bn + 40, 8, 96
     K = (S - 1) * kps + 64
-    plan = _plan_text("tiled", cfg)
+    plan = _plan_text(kind, cfg)
     text = hip_lib.describe_planned(plan, M, N, K, kps, S, inputs.DTYPES[dtype], layout=layout)
     print(f"case {layout} {dtype} M{M} N{N} K{K} kps{kps} S{S}: {text}", flush=True)
-    assert f"bm{bm} bn{bn}" in text and "grid288" in text, text
+    grid = "grid256 persistent" if kind == "tiledp" else "grid288"
+    assert f"bm{bm} bn{bn}" in text and grid in text, text
     stored = (lambda t: t) if layout == "nk" else (lambda t: t.T.contiguous())
     dev = torch.device("cuda:0")
     ea, eb = inputs.exact_operands(M, N, K, dtype, seed=bm + bn + S)
@@ -220,3 +230,48 @@ def test_tiled_split_fastest_exact(hip_lib, case):
     np.testing.assert_array_equal(c[: M * N], EC)
     guard_c = inputs.stored_bits(inputs.guarded_buffer(0, "nan", dtype=out))
     assert np.all(c[M * N:] == guard_c)
+
+
+# Persistent configurations with four or five tiles per workgroup (8 x 17
+# tiles x 8 splits = 1088 on 256 workgroups), splits of two chunks (the
+# second half empty for 16-bit inputs, so it is loaded through the zero
+# piece and the re-read pieces), a 40-column last tile and a one-chunk last
+# split; and 256x256 tiles at a split length of 10 and 16 chunks.  Exact-
+# arithmetic inputs: every partial and the sum match the binary64 reference
+# bit for bit.
+PERSISTENT_MANY = ([(c, "bf16", 96) for c in TILED_PT] +
+                   [(TILED_PT[0], "f16", 96), (TILED_PT[0], "f32", 96),
+                    (TILED_PT[0], "bf16", 608), (TILED_PT[0], "bf16", 1024)])
+
+
+@pytest.mark.gpu
+@pytest.mark.skipif(not gpu_available(), reason="no GPU")
+@pytest.mark.parametrize("case", PERSISTENT_MANY,
+                         ids=lambda c: "tiledp," + ",".join(map(str, c[0])) + f"-{c[1]}-kps{c[2]}")
+def test_persistent_many_tiles_exact(hip_lib, case):
+    cfg, dtype, kps = case
+    bm, bn = cfg[0], cfg[1]
+    M, N, S = 2048, 16 * 256 + 40, 8
+    K = (S - 1) * kps + 64
+    plan = _plan_text("tiledp", cfg)
+    text = hip_lib.describe_planned(plan, M, N, K, kps, S, inputs.DTYPES[dtype])
+    print(f"case {dtype} M{M} N{N} K{K} kps{kps} S{S}: {text}", flush=True)
+    assert text.endswith("grid256 persistent"), text
+    dev = torch.device("cuda:0")
+    ea, eb = inputs.exact_operands(M, N, K, dtype, seed=bm + bn + kps)
+    ea64 = oracle.decode(inputs.stored_bits(ea), dtype)
+    eb64 = oracle.decode(inputs.stored_bits(eb), dtype)
+    EP, _, _ = oracle.splitk_partials(ea64, eb64, kps, S)
+    EC = EP.sum(axis=0)
+    guard = np.float32(inputs.GUARD_VALUE).view(np.uint32)
+    for poison in ("nan", "seven"):
+        pbuf = inputs.guarded_buffer(S * M * N, poison).to(dev)
+        cbuf = inputs.guarded_buffer(M * N, poison).to(dev)
+        hip_lib.gemm_planned(plan, ea.to(dev), eb.to(dev), pbuf[: S * M * N].view(S, M, N), kps, S,
+                             C=cbuf[: M * N].view(M, N))
+        torch.cuda.synchronize()
+        p, c = pbuf.cpu().numpy(), cbuf.cpu().numpy()
+        assert np.all(p[S * M * N:].view(np.uint32) == guard)
+        assert np.all(c[M * N:].view(np.uint32) == guard)
+        np.testing.assert_array_equal(p[: S * M * N].astype(np.float64), EP.reshape(-1))
+        np.testing.assert_array_equal(c[: M * N].astype(np.float64), EC.reshape(-1))

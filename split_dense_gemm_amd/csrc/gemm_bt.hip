@@ -796,14 +796,15 @@ __device__ __attribute__((aligned(64))) uint32_t kZeroPiece[4];
 // buffer ring, B as [N,K]).  One workgroup per CU walks a sequence of tiles
 // instead of ending after one, and its LDS ring runs on across tiles: the
 // next tile's first chunk is loaded while this tile's last chunk is
-// multiplied, its second one right after, and both land while this tile's
-// partials are being stored.  A wave's vector-memory operations complete in
-// the order it issued them (loads into LDS and stores alike), so once 64 or
-// more store instructions have been issued after those loads, a counter of
-// at most 63 outstanding operations means that the loads have landed: the
-// next tile starts multiplying while the last of its stores drain, where
-// the one-tile kernel pays a workgroup's start and its first chunk's full
-// latency once per tile.
+// multiplied, and lands while this tile's partials are being stored.  A
+// wave's vector-memory operations complete in the order it issued them
+// (loads into LDS and stores alike), so once 64 or more store instructions
+// have been issued after that load, a counter of at most 63 outstanding
+// operations means that it has landed: the next tile starts multiplying
+// while the last of its stores drain, where the one-tile kernel pays a
+// workgroup's start and its first chunk's full latency once per tile.
+// (Loading the second chunk before the stores as well, into the slot the
+// last chunk frees, was 2-4% slower: that pass then had nothing to load.)
 //
 // Tile sequence: the tiles are numbered as in the one-tile kernel (split
 // major; groups of GM row tiles sweep the column tiles) and each XCD takes a
@@ -903,9 +904,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bt_tiled_pt(const uint8_t* 
     // The DMA instructions [lo, hi) of chunk c of the load tile into ring
     // slot `slot`.  With c < 0 they are dummies: they re-read the load tile's
     // last issued chunk (chunk `last`, whose addresses are valid whatever
-    // make_half did) into a spare LDS area that nothing reads.  A pass with
-    // nothing to load then still issues the same instructions, so the MFMA
-    // sequence around them needs no branch.
+    // make_half did) into a spare LDS area that nothing reads.  The last
+    // pass of the last tile, which has nothing to load, then still issues
+    // the same instructions, so the MFMA sequence around them needs no
+    // branch.
     auto dma = [&](int slot, int c, int last, int lo, int hi) __attribute__((always_inline)) {
         const bool dummy = c < 0;
         const size_t off = (size_t)(dummy ? last : c) * kChunkBytes;
@@ -983,7 +985,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bt_tiled_pt(const uint8_t* 
         for (int i = 0; i < slot; ++i) __builtin_amdgcn_s_sleep(8);
     }
     int rb = 0;          // ring slot of this tile's chunk 0
-    bool lead = false;   // this tile's chunks 0 and 1 were issued before the last tile's stores
+    bool lead = false;   // this tile's chunk 0 was issued before the last tile's stores
     int issued = 0;      // last issued chunk of the load tile
     for (;;) {
         // The load tile is this tile until its last chunk is multiplied.
@@ -996,10 +998,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bt_tiled_pt(const uint8_t* 
             for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x16{};
         for (int c = 0; c < cn; ++c) {
             // Chunk c issues chunk c + 1, except that the last one issues the
-            // next tile's chunk 0 (which then becomes the load tile) and
-            // that in a tile whose chunk 1 went out before the last stores,
-            // chunk 0 issues dummies.  The last tile's last chunk issues
-            // dummies too.
+            // next tile's chunk 0 (which then becomes the load tile), or
+            // dummies in the last tile.
             int next_c = c + 1;
             if (c == cn - 1) {
                 next_c = -1;
@@ -1008,29 +1008,20 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bt_tiled_pt(const uint8_t* 
                     set_load_tile(s, mt, nt);
                     next_c = 0;
                 }
-            } else if (lead && c == 0) {
-                next_c = -1;
             }
             if (next_c >= 0) {
                 if (next_c == nch - 1 && k0 + next_c * CK + CK / 2 >= k1) make_half(next_c);
                 issued = next_c;
             }
-            // At least 64 stores were issued after a lead tile's chunks 0 and
-            // 1: with at most 63 operations outstanding, both have landed.
+            // At least 64 stores were issued after a lead tile's chunk 0: with
+            // at most 63 operations outstanding, it has landed.  Chunk 1 went
+            // out after the stores, so its wait covers them too.
             if (lead && c == 0)
                 __builtin_amdgcn_s_waitcnt(SPLITK_VMCNT(63));
-            else if (!(lead && c == 1))
+            else
                 __builtin_amdgcn_s_waitcnt(SPLITK_VMCNT(0));
             lds_barrier();
             compute((rb + c) & 1, (rb + c + 1) & 1, next_c, issued);
-        }
-        if (more) {
-            lds_barrier();  // every wave is done with the last chunk's slot
-            if (nch > 1) {
-                if (nch == 2 && k0 + CK + CK / 2 >= k1) make_half(1);
-                dma((rb + cn + 1) & 1, 1, 1, 0, DPW);
-                issued = 1;
-            }
         }
 
         float* base = P + ((size_t)cs * M + (size_t)cmt * BM + wm * TM + 4 * h) * N + (size_t)cnt * BN +

@@ -140,6 +140,39 @@ def exact_operands(M: int, N: int, K: int, dtype: str, seed: int):
     return a.to(DTYPES[dtype]).contiguous(), b.to(DTYPES[dtype]).contiguous()
 
 
+def product_factors(M: int, N: int, K: int, seed: int, a_max: int = 3, b_max: int = 5):
+    """Seeded integer factors (a[M], b[N], u[K], v[K]) of the operands
+    A[i,k] = a[i]*u[k] and B[j,k] = b[j]*v[k] (``product_operands``).
+
+    a[i] is drawn from +-1..a_max, b[j] from +-1..b_max, u[k] and v[k] from
+    {-1, 0, 1}, all uniformly; CPU int64 tensors.  Every operand entry is then
+    an integer of magnitude at most a_max or b_max, exact in F32, F16 and BF16.
+    """
+    gen = torch.Generator().manual_seed(seed)
+
+    def signed(n, top):
+        mag = torch.randint(1, top + 1, (n,), generator=gen)
+        return mag * (torch.randint(0, 2, (n,), generator=gen) * 2 - 1)
+
+    a = signed(M, a_max)
+    b = signed(N, b_max)
+    u = torch.randint(-1, 2, (K,), generator=gen)
+    v = torch.randint(-1, 2, (K,), generator=gen)
+    return a, b, u, v
+
+
+def product_operands(factors, dtype: str, device, b_layout: str = "nk"):
+    """A[M,K] = a (x) u and B = b (x) v from ``product_factors``, built directly
+    in element type `dtype` on `device` (each entry is one exact product of two
+    small integers).  B is [N,K] for b_layout "nk" and [K,N] for "kn"."""
+    a, b, u, v = factors
+    t = DTYPES[dtype]
+    a_, b_, u_, v_ = (x.to(device=device, dtype=t) for x in (a, b, u, v))
+    A = torch.outer(a_, u_).contiguous()
+    B = torch.outer(b_, v_) if b_layout == "nk" else torch.outer(v_, b_)
+    return A, B.contiguous()
+
+
 def guarded_buffer(n: int, poison: str = "seven", dtype: str = "f32") -> torch.Tensor:
     """CPU buffer of n poisoned elements of `dtype` plus GUARD_COUNT trailing guards."""
     buf = torch.empty(n + GUARD_COUNT, dtype=DTYPES[dtype])

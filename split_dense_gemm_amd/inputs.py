@@ -98,6 +98,17 @@ PAGE_SHAPES = (
 
 WORKLOADS = {w.name: w for w in CONFIGS + PAGE_SHAPES}
 
+# Shapes whose N the column tile does not divide (the N-tail tiles), for the
+# measurements of the calls beyond the fixed chain: the headline and large
+# shapes with N cut below a multiple of 64 and of 256, and skinny F16 and F32
+# cases.  Same recipe as above.
+NTAIL_SHAPES = (
+    Workload("bf16_m256_n1000_k2048_s2", "bf16", 256, 1000, 2048, 1024, 2, seed=1260),
+    Workload("f16_m32_n520_k2080_s4", "f16", 32, 520, 2080, 544, 4, seed=1261),
+    Workload("f32_m96_n504_k2048_s4", "f32", 96, 504, 2048, 512, 4, seed=1262),
+    Workload("bf16_m2048_n4000_k4096_s8", "bf16", 2048, 4000, 4096, 512, 8, dist="normal", seed=1263),
+)
+
 HEADLINE = "bf16_m256_n1024_k2048_s2"
 
 

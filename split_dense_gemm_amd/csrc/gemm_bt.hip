@@ -1480,8 +1480,13 @@ static GemmPlan plan_by_shape(int dtype, int64_t M, int64_t N, int64_t K, int64_
     // Large problems: 256x256 tiles (2x2 waves) when there is at least one
     // per CU, else 256x128 tiles on 2x4 waves (two waves per SIMD, measured
     // 5-8% faster than 2x2 for this tile); these read the least L2 data per
-    // flop.  An N that 256 does not divide takes 256x128 tiles, the last one
-    // a tail.
+    // flop.  For 16-bit inputs an N that 256 does not divide counts its
+    // narrowed last column tile as a whole one and follows the same rules:
+    // over twelve such shapes (N 2000-8000, N mod 256 from 8 to 216, 2-8
+    // splits) 256x256 tiles ran the chain at 0.87-1.02x the 256x128 time
+    // with B as [N,K] where the rules below pick them (0.97x at geometric
+    // mean; 0.99-1.04x on the three half-full last rounds that they leave
+    // to 256x128 tiles), and at 0.80-0.97x with B as [K,N].
     //
     // With B as [N,K], 256x128 tiles also take over where the last round of
     // 256x256 ones would be at most half full (workgroups mod 256 CUs in
@@ -1529,8 +1534,8 @@ static GemmPlan plan_by_shape(int dtype, int64_t M, int64_t N, int64_t K, int64_
         return GemmPlan{kTiled, best->bm, best->bn, best->wm * best->wn, best->wm, best_wg,
                         best->wm * best->wn * 64, layout, tiled_nbuf(best->bm, best->bn)};
     }
-    if (M % 256 == 0 && N % 256 == 0 && (M / 256) * (N / 256) * splits >= 256) {
-        const int64_t wg = (M / 256) * (N / 256) * splits;
+    if (M % 256 == 0 && (M / 256) * cdiv(N, 256) * splits >= 256) {
+        const int64_t wg = (M / 256) * cdiv(N, 256) * splits;
         const bool half_round = wg % 256 != 0 && wg % 256 <= 128;
         const bool short_last_round =
             layout == kLayoutNK && half_round &&

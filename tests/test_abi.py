@@ -238,9 +238,23 @@ def test_n_tails_accepted(hip_lib, N, status_nk, status_kn):
 
 
 def test_tail_tiles_in_plans(hip_lib):
-    # Column tiles are counted with the narrowed last tile included.
-    text = hip_lib.describe(2048, 4000, 1024, 256, 4, BF16)
-    assert text.startswith("tiled bm256 bn128") and text.endswith(f"grid{8 * 32 * 4}"), text
+    # Column tiles are counted with the narrowed last tile included: 16-bit
+    # inputs take 256x256 tiles by the same rules as an N that 256 divides
+    # (persistent with B as [N,K] over several rounds of short splits) ...
+    assert hip_lib.describe_bn(2048, 4000, 1024, 256, 4, BF16) == (
+        f"tiled bm256 bn256 waves2x2 ring2 block256 grid{8 * 16 * 4}")
+    assert hip_lib.describe(2048, 4000, 1024, 256, 4, BF16) == (
+        "tiled bm256 bn256 waves2x2 ring2 block256 grid256 persistent")
+    assert hip_lib.describe(2048, 2000, 4096, 1024, 4, BF16) == (
+        f"tiled bm256 bn256 waves2x2 ring2 block256 grid{8 * 8 * 4}")
+    # ... and 256x128 tiles where the last round of 256x256 ones would be at
+    # most half full (B as [N,K]): 384 of them in two splits.
+    text = hip_lib.describe(4096, 3000, 2048, 1024, 2, BF16)
+    assert text.startswith("tiled bm256 bn128") and text.endswith(f"grid{16 * 24 * 2}"), text
+    assert hip_lib.describe_bn(4096, 3000, 2048, 1024, 2, BF16) == (
+        f"tiled bm256 bn256 waves2x2 ring2 block256 grid{16 * 12 * 2}")
+    # F32 keeps 256x256 tiles to an N that 256 divides.
+    assert " bn256 " not in hip_lib.describe(2048, 4000, 1024, 256, 4, 0)
     text = hip_lib.describe(64, 100, 1024, 256, 4, BF16)
     assert f" grid{2 * (2 if ' bn64 ' in text else 4) * 4}" in text, text
 

@@ -6,8 +6,9 @@ Each case below comes within a few thousand elements of one or more of those
 limits, so an offset computed in 32 bits anywhere in a kernel would wrap and
 land on the wrong element (or outside the buffer).  The cases take the kernel
 families the planner uses at such sizes: the persistent 256x256 kernel, the
-one-tile 256x256 kernel of B stored [K,N], 256x128 tiles with a 64-column
-tail, the skinny LDS-DMA kernel on a million workgroups, and the
+one-tile 256x256 kernel of B stored [K,N], both with narrowed last column
+tiles too, 256x128 tiles with a 64-column tail, the skinny LDS-DMA kernel on
+a million workgroups, and the
 register-staged skinny kernel on 32 splits of a million k each.
 
 Operands are exact products of seeded small integers, A[i,k] = a[i]*u[k] and
@@ -46,8 +47,11 @@ CASES = [
     ("persistent_f32", 11008, 97536, 256, 128, 2, "f32", "nk", "persistent"),
     # the same with B stored [K,N]: one 256x256 tile per workgroup
     ("kn", 11008, 97536, 256, 128, 2, "bf16", "kn", "tiled bm256 bn256"),
-    # splits*M*N = 2,145,386,496: 256x128 tiles, the last column tile 64 wide
-    ("tail", 8192, 65472, 128, 32, 4, "bf16", "nk", "tiled bm256 bn128"),
+    # splits*M*N = 2,145,386,496: the persistent kernel, the last column tile 192 wide
+    ("persistent_tail", 8192, 65472, 128, 32, 4, "bf16", "nk", "persistent"),
+    # splits*M*N = 2,136,997,888: 256x128 tiles (the last round of 256x256
+    # ones would be half full), the last column tile 64 wide
+    ("tail", 8192, 65216, 128, 32, 4, "bf16", "nk", "tiled bm256 bn128"),
     # splits*M*N = M*K = 2,147,479,552: 1,048,574 workgroups
     ("tall", 16777184, 64, 128, 64, 2, "bf16", "nk", "wavekdma"),
     # N*K = 2,147,481,600 (rows of 64 MiB): 32 splits of 2^20

@@ -15,7 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libsplitk.so")
-SOURCES = ["gemm_bt.hip", "slab_reduce.hip", "split_choice.cpp", "splitk_api.cpp", "static_slabs.hip"]
+SOURCES = ["gemm_bt.hip", "plan.cpp", "slab_reduce.hip", "split_choice.cpp", "splitk_api.cpp", "static_slabs.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops keeps the compiler from forming packed F32 VALU ops.

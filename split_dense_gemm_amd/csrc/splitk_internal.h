@@ -6,6 +6,9 @@
 
 namespace splitk {
 
+// One chunk of K: 128 bytes of a row (8 pieces of 16 bytes).
+constexpr int kChunkBytes = 128;
+
 // Which GEMM kernel family serves a call.
 enum GemmKind : int {
     // Skinny shapes (few output tiles): the W waves of a workgroup take the
@@ -97,6 +100,20 @@ constexpr int64_t kStaticSlabFloats = int64_t(16) << 20;
 // first call per device (hipGetSymbolAddress) and cached; NULL if the
 // lookup fails.
 float* static_slabs();
+
+// Default ring depth of a tile: as many buffers as fit in 160 KiB, up to four.
+constexpr int tiled_nbuf(int bm, int bn) {
+    return (160 * 1024) / ((bm + bn) * kChunkBytes) > 4 ? 4 : (160 * 1024) / ((bm + bn) * kChunkBytes);
+}
+
+// Compute units of the current device (looked up once per device).
+int device_cus();
+
+// Whether a kernel configuration is instantiated (the lists in gemm_bt.hip).
+bool wavekdma_config_exists(int bm, int bn, int w, int r);
+bool wavek_config_exists(int layout, int bm, int bn, int w, int d);
+bool tiled_pt_config_exists(int layout, int bm, int bn, int wm, int wn);
+bool tiled_config_exists(int layout, int bm, int bn, int wm, int wn, int nbuf);
 
 // Chooses the kernel configuration for a validated problem.
 GemmPlan plan_gemm(int dtype, int64_t M, int64_t N, int64_t K, int64_t kps, int64_t splits,

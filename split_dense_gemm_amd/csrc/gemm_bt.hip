@@ -778,7 +778,8 @@ hipError_t launch_tiled(const void* A, const void* B, float* P, int64_t M, int64
 __device__ __attribute__((aligned(64))) uint32_t kZeroPiece[4];
 
 // Persistent form of the large-tile kernel for grids of several rounds (two-
-// buffer ring, B as [N,K]).  One workgroup per CU walks a sequence of tiles
+// buffer ring; B as [N,K], or as [K,N] with BL = 1, staged and read as in
+// the one-tile kernel).  One workgroup per CU walks a sequence of tiles
 // instead of ending after one, and its LDS ring runs on across tiles: the
 // next tile's first chunk is loaded while this tile's last chunk is
 // multiplied, and lands while this tile's partials are being stored.  A
@@ -798,7 +799,7 @@ __device__ __attribute__((aligned(64))) uint32_t kZeroPiece[4];
 // takes tiles j, j + wg_x, j + 2 wg_x, ... of that range.  This is a
 // bijection onto all tiles as long as every XCD has a workgroup (gridDim.x
 // >= 8) and no XCD has more workgroups than tiles (gridDim.x <= tiles).
-template <int DT, int BM, int BN, int WM, int WN>
+template <int DT, int BM, int BN, int WM, int WN, int BL>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_bt_tiled_pt(const uint8_t* __restrict__ A,
                                                                  const uint8_t* __restrict__ B,
                                                                  float* __restrict__ P, int M, int N,
@@ -816,6 +817,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bt_tiled_pt(const uint8_t* 
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int MB = TM / 32, NB = TN / 32;
     constexpr int GM = 4;
+    // [K,N]: DMA instructions [IA, DPW) fill the B part, [IH, DPW) its second
+    // half of the k-rows.
+    constexpr int IA = BM / 8 / NW, IH = (BM + BN / 2) / 8 / NW;
     // A whole sub-tile's partial store is MB * 16 * NB store instructions per
     // wave; the wait at the start of the next tile counts on at least 64.
     static_assert(MB * 16 * NB >= 64, "tile too small for the cross-tile wait");
@@ -849,6 +853,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bt_tiled_pt(const uint8_t* 
     const int r = lane & 31;
     const int h = lane >> 5;
     const size_t row_bytes = (size_t)K * ES;
+    const size_t row_bytes_b = (size_t)N * ES;  // [K,N] layout: one k-row of B
 
     // Chunk-0 address of each DMA instruction of this wave, piece folded in,
     // for the tile whose chunks are being loaded (the "load tile"), and that
@@ -862,10 +867,15 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bt_tiled_pt(const uint8_t* 
 #pragma unroll
         for (int i = 0; i < DPW; ++i) {
             const int row = 8 * (i * NW + wave) + (lane >> 3);
-            const uint8_t* src = (row < BM ? A + (size_t)(mt * BM + row) * row_bytes
-                                           : B + (size_t)min(nt * BN + row - BM, N - 1) * row_bytes) +
-                                 (size_t)k0 * ES;
-            full[i] = src + slot_of(row, lane & 7) * 16;
+            if (BL == 1 && i >= IA) {
+                full[i] = B + (size_t)k0 * row_bytes_b +
+                          kn_src<ES, BN>(row - BM, lane & 7, row_bytes_b, (size_t)nt * BN * ES);
+            } else {
+                const uint8_t* src = (row < BM ? A + (size_t)(mt * BM + row) * row_bytes
+                                               : B + (size_t)min(nt * BN + row - BM, N - 1) * row_bytes) +
+                                     (size_t)k0 * ES;
+                full[i] = src + slot_of(row, lane & 7) * 16;
+            }
         }
     };
     // A half-empty chunk is always the load tile's last: before it is issued
@@ -875,15 +885,22 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bt_tiled_pt(const uint8_t* 
     // 2 of a lane's piece is the same in every instruction: slot_of(8g +
     // lane/8, lane%8) differs between row groups g only in bit 0.
     const bool upper = (slot_of(lane >> 3, lane & 7) & 4) != 0;
+    // With B as [K,N] the instructions of the second half of the k-rows
+    // re-read the first half instead (in bounds, finite, and met by the zero
+    // upper half of the A rows).
     auto make_half = [&](int c) __attribute__((always_inline)) {
         if (upper) {
 #pragma unroll
             for (int i = 0; i < DPW; ++i) {
                 if (8 * (i * NW + wave) < BM)
                     full[i] = (const uint8_t*)((uintptr_t)kZeroPiece - (uintptr_t)c * kChunkBytes);
-                else
+                else if (BL == 0)
                     full[i] -= 64;
             }
+        }
+        if (BL == 1) {
+#pragma unroll
+            for (int i = IH; i < DPW; ++i) full[i] -= (size_t)(CK / 2) * row_bytes_b;
         }
     };
     // The DMA instructions [lo, hi) of chunk c of the load tile into ring
@@ -895,12 +912,14 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bt_tiled_pt(const uint8_t* 
     // branch.
     auto dma = [&](int slot, int c, int last, int lo, int hi) __attribute__((always_inline)) {
         const bool dummy = c < 0;
-        const size_t off = (size_t)(dummy ? last : c) * kChunkBytes;
+        const int cc = dummy ? last : c;
+        const size_t off = (size_t)cc * kChunkBytes;
+        const size_t off_kn = (size_t)cc * CK * row_bytes_b;  // [K,N]: CK k-rows per chunk
         uint8_t* dst = dummy ? smem + NBUF * BUF + wave * 1024 : smem + slot * BUF + wave * 1024;
         const int step = dummy ? 0 : NW * 1024;
 #pragma unroll
         for (int i = lo; i < hi; ++i) {
-            const uint8_t* g = full[i] + off;
+            const uint8_t* g = full[i] + ((BL == 1 && i >= IA) ? off_kn : off);
             __builtin_amdgcn_global_load_lds((const void*)g, (__attribute__((address_space(3))) void*)(dst + i * step),
                                              16, 0, 0);
         }
@@ -924,11 +943,15 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bt_tiled_pt(const uint8_t* 
             }
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
-                const int row = BM + wn * TN + nb * 32 + r;
-                fb[q & 1][nb] = *(const u32x4*)(lds + row * kChunkBytes + slot_of(row, 2 * q + h) * 16);
+                if (BL == 1) {
+                    fb[q & 1][nb] = kn_frag<DT, BN>(lds + BM * kChunkBytes, q, wn * (TN / 32) + nb, lane);
+                } else {
+                    const int row = BM + wn * TN + nb * 32 + r;
+                    fb[q & 1][nb] = *(const u32x4*)(lds + row * kChunkBytes + slot_of(row, 2 * q + h) * 16);
+                }
             }
         };
-        constexpr int NREAD = MB + NB;
+        constexpr int NREAD = MB + NB * (BL == 1 ? (DT == 0 ? 4 : 2) : 1);  // LDS reads per step
         constexpr int NM = Op::kStepsPerPiece * MB * NB;
         constexpr int DMA_STEPS = 2;
         frags(std::integral_constant<int, 0>{});
@@ -1056,7 +1079,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bt_tiled_pt(const uint8_t* 
     }
 }
 
-template <int DT, int BM, int BN, int WM, int WN>
+template <int DT, int BM, int BN, int WM, int WN, int BL>
 hipError_t launch_tiled_pt(const void* A, const void* B, float* P, int64_t M, int64_t N, int64_t K,
                            int64_t kps, int64_t splits, hipStream_t stream) {
     const int tiles_m = (int)(M / BM), tiles_n = (int)((N + BN - 1) / BN);
@@ -1071,7 +1094,7 @@ hipError_t launch_tiled_pt(const void* A, const void* B, float* P, int64_t M, in
     int streaming = stream_slabs(splits, M, N) ? 1 : 0;
     int stagger = tiles > g ? (int)g : 0;
     void* args[] = {&a, &b, &P, &m, &n, &k, &kp, (void*)&tiles_m, (void*)&tiles_n, &sp, &streaming, &stagger};
-    return hipLaunchKernel((const void*)&gemm_bt_tiled_pt<DT, BM, BN, WM, WN>, grid, block, args, 0, stream);
+    return hipLaunchKernel((const void*)&gemm_bt_tiled_pt<DT, BM, BN, WM, WN, BL>, grid, block, args, 0, stream);
 }
 
 // Instantiated shared-ring configurations: (BM, BN, WM, WN, NBUF), NBUF
@@ -1087,6 +1110,8 @@ hipError_t launch_tiled_pt(const void* A, const void* B, float* P, int64_t M, in
     X(256, 256, 2, 2)              \
     X(256, 128, 2, 2)              \
     X(256, 128, 2, 4)
+#define SPLITK_KN_TILED_PT_CONFIGS(X) \
+    X(256, 256, 2, 2)
 
 // Skinny kernel with the last chunk by LDS DMA.  Same work split as
 // gemm_bt_wavek (waves take a split's chunks round-robin, partial tiles
@@ -1325,6 +1350,14 @@ hipError_t launch_dtype_kn(const GemmPlan& p, const void* A, const void* B, floa
         SPLITK_KN_WAVEK_CONFIGS(X)
 #undef X
     }
+    if (p.kind == kTiled && p.persist) {
+#define X(cbm, cbn, cwm, cwn)                                                     \
+    if (p.bm == cbm && p.bn == cbn && p.waves == cwm * cwn && p.stages == cwm)    \
+        return launch_tiled_pt<DT, cbm, cbn, cwm, cwn, 1>(A, B, P, M, N, K, kps, splits, st);
+        SPLITK_KN_TILED_PT_CONFIGS(X)
+#undef X
+        return hipErrorInvalidConfiguration;
+    }
     if (p.kind == kTiled) {
 #define X(cbm, cbn, cwm, cwn, cnb)                                                \
     if (p.bm == cbm && p.bn == cbn && p.waves == cwm * cwn && p.stages == cwm &&  \
@@ -1357,7 +1390,7 @@ hipError_t launch_dtype(const GemmPlan& p, const void* A, const void* B, float* 
     if (p.kind == kTiled && p.persist) {
 #define X(cbm, cbn, cwm, cwn)                                                     \
     if (p.bm == cbm && p.bn == cbn && p.waves == cwm * cwn && p.stages == cwm)    \
-        return launch_tiled_pt<DT, cbm, cbn, cwm, cwn>(A, B, P, M, N, K, kps, splits, st);
+        return launch_tiled_pt<DT, cbm, cbn, cwm, cwn, 0>(A, B, P, M, N, K, kps, splits, st);
         SPLITK_TILED_PT_CONFIGS(X)
 #undef X
         return hipErrorInvalidConfiguration;
@@ -1396,9 +1429,12 @@ bool wavek_config_exists(int layout, int bm, int bn, int w, int d) {
 }
 
 bool tiled_pt_config_exists(int layout, int bm, int bn, int wm, int wn) {
-    if (layout != kLayoutNK) return false;
 #define X(cbm, cbn, cwm, cwn) \
     if (bm == cbm && bn == cbn && wm == cwm && wn == cwn) return true;
+    if (layout == kLayoutKN) {
+        SPLITK_KN_TILED_PT_CONFIGS(X)
+        return false;
+    }
     SPLITK_TILED_PT_CONFIGS(X)
 #undef X
     return false;

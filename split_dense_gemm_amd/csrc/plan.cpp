@@ -223,16 +223,18 @@ GemmPlan plan_gemm(int dtype, int64_t M, int64_t N, int64_t K, int64_t kps, int6
             p = big;
     }
     p.order = tile_order(p, dtype, M, N, K, kps, splits);
-    // Grids of several rounds of 256x256 tiles, B as [N,K], splits of at
-    // most 16 chunks: the persistent kernel, which starts each CU's next tile
-    // while the last one's partials are still being stored.  Measured on
-    // BF16 2048x4096 at 8 splits against the one-tile kernel: 0.92x at 4
-    // chunks per split, 0.94-0.97x at 8 (the 2048x4096x4096 workload),
-    // 0.98x at 16, 1.01x at 32; 4096x4096x4096 at 8 splits 0.98x, F16
-    // 0.97x, F32 0.99x.
+    // Grids of several rounds of 256x256 tiles, splits of at most 16 chunks:
+    // the persistent kernel, which starts each CU's next tile while the last
+    // one's partials are still being stored.  Measured on BF16 2048x4096 at
+    // 8 splits against the one-tile kernel, B as [N,K]: 0.92x at 4 chunks
+    // per split, 0.94-0.97x at 8 (the 2048x4096x4096 workload), 0.98x at 16,
+    // 1.01x at 32; 4096x4096x4096 at 8 splits 0.98x, F16 0.97x, F32 0.99x.
+    // B as [K,N], GEMM alone: 0.93x at 4 chunks (2048x4096x2048 in 8
+    // splits), 0.96-0.97x at 8 (2048x4096x4096, 2048x4000x4096,
+    // 4096x4096x4096 in 8 splits), 0.98-1.00x at 16.
     const int64_t es = dtype == 0 ? 4 : 2;
-    if (p.kind == kTiled && p.layout == kLayoutNK && p.bm == 256 && p.bn == 256 && p.waves == 4 &&
-        p.stages == 2 && p.order == 0 && p.grid > device_cus() && (kps * es + 127) / 128 <= 16)
+    if (p.kind == kTiled && p.bm == 256 && p.bn == 256 && p.waves == 4 && p.stages == 2 &&
+        p.order == 0 && p.grid > device_cus() && (kps * es + 127) / 128 <= 16)
         p.persist = 1;
     return p;
 }

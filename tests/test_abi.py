@@ -240,9 +240,9 @@ def test_n_tails_accepted(hip_lib, N, status_nk, status_kn):
 def test_tail_tiles_in_plans(hip_lib):
     # Column tiles are counted with the narrowed last tile included: 16-bit
     # inputs take 256x256 tiles by the same rules as an N that 256 divides
-    # (persistent with B as [N,K] over several rounds of short splits) ...
+    # (persistent over several rounds of short splits) ...
     assert hip_lib.describe_bn(2048, 4000, 1024, 256, 4, BF16) == (
-        f"tiled bm256 bn256 waves2x2 ring2 block256 grid{8 * 16 * 4}")
+        "tiled bm256 bn256 waves2x2 ring2 block256 grid256 persistent")
     assert hip_lib.describe(2048, 4000, 1024, 256, 4, BF16) == (
         "tiled bm256 bn256 waves2x2 ring2 block256 grid256 persistent")
     assert hip_lib.describe(2048, 2000, 4096, 1024, 4, BF16) == (
@@ -252,7 +252,9 @@ def test_tail_tiles_in_plans(hip_lib):
     text = hip_lib.describe(4096, 3000, 2048, 1024, 2, BF16)
     assert text.startswith("tiled bm256 bn128") and text.endswith(f"grid{16 * 24 * 2}"), text
     assert hip_lib.describe_bn(4096, 3000, 2048, 1024, 2, BF16) == (
-        f"tiled bm256 bn256 waves2x2 ring2 block256 grid{16 * 12 * 2}")
+        "tiled bm256 bn256 waves2x2 ring2 block256 grid256 persistent")
+    assert hip_lib.describe_bn(4096, 3944, 2048, 2048, 1, BF16) == (
+        f"tiled bm256 bn256 waves2x2 ring2 block256 grid{16 * 16}")  # one round
     # F32 keeps 256x256 tiles to an N that 256 divides.
     assert " bn256 " not in hip_lib.describe(2048, 4000, 1024, 256, 4, 0)
     text = hip_lib.describe(64, 100, 1024, 256, 4, BF16)
@@ -344,12 +346,12 @@ def test_short_last_round_takes_256x128_tiles(hip_lib):
         wg = (shape[0] // 256) * (shape[1] // 256) * shape[4]
         assert not (256 < wg <= 384 and shape[4] <= 2), shape
         # Several rounds of splits of at most 16 chunks run persistently on
-        # 256 workgroups (B as [N,K] only).
+        # 256 workgroups (both B layouts).
         persistent = wg > 256 and shape[3] * 2 // 128 <= 16
-        assert hip_lib.describe(*shape, BF16) == (
-            "tiled bm256 bn256 waves2x2 ring2 block256 grid256 persistent" if persistent
-            else f"tiled bm256 bn256 waves2x2 ring2 block256 grid{wg}"), shape
-        assert hip_lib.describe_bn(*shape, BF16).startswith(f"tiled bm256 bn256 waves2x2 ring2 block256 grid{wg}")
+        want = ("tiled bm256 bn256 waves2x2 ring2 block256 grid256 persistent" if persistent
+                else f"tiled bm256 bn256 waves2x2 ring2 block256 grid{wg}")
+        assert hip_lib.describe(*shape, BF16) == want, shape
+        assert hip_lib.describe_bn(*shape, BF16) == want, shape
     # F32: the tile with the fewest rounds x tile area x per-tile factor
     # (256x256 1, 256x128 1.05, 128x128 1.1) among the three (B as [K,N]: no
     # 128x128); the same shapes in BF16 (24 chunks per split) keep 256x256.
@@ -372,10 +374,10 @@ def test_short_last_round_takes_256x128_tiles(hip_lib):
 
 
 def test_persistent_large_tiles_rule(hip_lib):
-    """256x256 tiles with B as [N,K] run persistently (one workgroup per CU
-    walking several tiles) where there are more tiles than CUs and every
-    split is at most 16 chunks; one round, longer splits, B as [K,N] and the
-    other tiles keep one workgroup per tile."""
+    """256x256 tiles run persistently (one workgroup per CU walking several
+    tiles), with either B layout, where there are more tiles than CUs and
+    every split is at most 16 chunks; one round, longer splits and the other
+    tiles keep one workgroup per tile."""
     yes = [((2048, 4096, 4096, 512, 8), BF16), ((2048, 4096, 4096, 512, 8), 1),
            ((2048, 4096, 4096, 512, 8), 0), ((2048, 4096, 4096, 1024, 4), BF16),
            ((4096, 4096, 4096, 256, 16), BF16)]
@@ -385,9 +387,10 @@ def test_persistent_large_tiles_rule(hip_lib):
           ((256, 1024, 2048, 1024, 2), BF16)]     # skinny
     for shape, dt in yes:
         assert hip_lib.describe(*shape, dt).endswith("grid256 persistent"), (shape, dt)
-        assert "persistent" not in hip_lib.describe_bn(*shape, dt), (shape, dt)
+        assert hip_lib.describe_bn(*shape, dt).endswith("grid256 persistent"), (shape, dt)
     for shape, dt in no:
         assert "persistent" not in hip_lib.describe(*shape, dt), (shape, dt)
+        assert "persistent" not in hip_lib.describe_bn(*shape, dt), (shape, dt)
     # Named: "tiledp" is the persistent form, "tiled" never is; fewer tiles
     # than CUs launch one workgroup per tile.
     assert hip_lib.describe_planned("tiled,256,256,2,2", 2048, 4096, 4096, 512, 8, BF16).endswith("grid1024")
@@ -419,7 +422,8 @@ PLAN_CASES = [
     ("wavek,32,64,8,2", 0, (256, 1024, 2048, 1024, 3, BF16), SPLIT),
     ("tiledp,256,256,2,2", 0, (2048, 4096, 4096, 512, 8, BF16), OK),
     ("tiledp,256,128,2,4", 0, (512, 1024, 2048, 256, 8, BF16), OK),
-    ("tiledp,256,256,2,2", 1, (2048, 4096, 4096, 512, 8, BF16), PLAN),   # no [K,N] form
+    ("tiledp,256,256,2,2", 1, (2048, 4096, 4096, 512, 8, BF16), OK),     # [K,N] form
+    ("tiledp,256,128,2,4", 1, (512, 1024, 2048, 256, 8, BF16), PLAN),    # no [K,N] 256x128 form
     ("tiledp,256,256,2,2,2", 0, (2048, 4096, 4096, 512, 8, BF16), PLAN), # no ring argument
     ("tiledp,128,128,2,2", 0, (2048, 4096, 4096, 512, 8, BF16), PLAN),   # not instantiated
     ("tiledp,256,256,2,2", 0, (256, 512, 2048, 1024, 2, BF16), PLAN),    # 4 tiles: an XCD without one

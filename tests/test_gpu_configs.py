@@ -44,6 +44,7 @@ TILED = _configs("SPLITK_TILED_CONFIGS")
 KN_WAVEK = _configs("SPLITK_KN_WAVEK_CONFIGS")
 KN_TILED = _configs("SPLITK_KN_TILED_CONFIGS")
 TILED_PT = _configs("SPLITK_TILED_PT_CONFIGS")
+KN_TILED_PT = _configs("SPLITK_KN_TILED_PT_CONFIGS")
 
 
 def _shape(kind, cfg):
@@ -66,7 +67,8 @@ def _shape(kind, cfg):
 
 CASES = ([("nk", "wavek", c) for c in WAVEK] + [("nk", "wavekdma", c) for c in WAVEKDMA] +
          [("nk", "tiled", c) for c in TILED] + [("kn", "wavek", c) for c in KN_WAVEK] +
-         [("kn", "tiled", c) for c in KN_TILED] + [("nk", "tiledp", c) for c in TILED_PT])
+         [("kn", "tiled", c) for c in KN_TILED] + [("nk", "tiledp", c) for c in TILED_PT] +
+         [("kn", "tiledp", c) for c in KN_TILED_PT])
 
 
 def _plan_text(kind, cfg):
@@ -144,7 +146,8 @@ def test_config_parity(hip_lib, case, dtype):
 MULTI_ROUND = ([("nk", "tiled", c, "bf16") for c in TILED] + [("kn", "tiled", c, "bf16") for c in KN_TILED] +
                [("nk", "tiled", TILED[0], "f16"), ("nk", "tiled", TILED[0], "f32")] +
                [("nk", "tiledp", c, "bf16") for c in TILED_PT] +
-               [("nk", "tiledp", TILED_PT[0], "f16"), ("nk", "tiledp", TILED_PT[0], "f32")])
+               [("nk", "tiledp", TILED_PT[0], "f16"), ("nk", "tiledp", TILED_PT[0], "f32")] +
+               [("kn", "tiledp", c, dt) for c in KN_TILED_PT for dt in ("bf16", "f16", "f32")])
 
 
 @pytest.mark.gpu
@@ -236,27 +239,31 @@ def test_tiled_split_fastest_exact(hip_lib, case):
 # tiles x 8 splits = 1088 on 256 workgroups), splits of two chunks (the
 # second half empty for 16-bit inputs, so it is loaded through the zero
 # piece and the re-read pieces), a 40-column last tile and a one-chunk last
-# split; and 256x256 tiles at a split length of 10 and 16 chunks.  Exact-
-# arithmetic inputs: every partial and the sum match the binary64 reference
-# bit for bit.
-PERSISTENT_MANY = ([(c, "bf16", 96) for c in TILED_PT] +
-                   [(TILED_PT[0], "f16", 96), (TILED_PT[0], "f32", 96),
-                    (TILED_PT[0], "bf16", 608), (TILED_PT[0], "bf16", 1024)])
+# split; and 256x256 tiles at a split length of 10 and 16 chunks; both B
+# layouts (with B as [K,N] the empty half of a two-chunk split re-reads the
+# first half of its k-rows).  Exact-arithmetic inputs: every partial and the
+# sum match the binary64 reference bit for bit.
+PERSISTENT_MANY = ([("nk", c, "bf16", 96) for c in TILED_PT] +
+                   [("nk", TILED_PT[0], "f16", 96), ("nk", TILED_PT[0], "f32", 96),
+                    ("nk", TILED_PT[0], "bf16", 608), ("nk", TILED_PT[0], "bf16", 1024)] +
+                   [("kn", c, dt, 96) for c in KN_TILED_PT for dt in ("bf16", "f16", "f32")] +
+                   [("kn", KN_TILED_PT[0], "bf16", 608), ("kn", KN_TILED_PT[0], "bf16", 1024)])
 
 
 @pytest.mark.gpu
 @pytest.mark.skipif(not gpu_available(), reason="no GPU")
 @pytest.mark.parametrize("case", PERSISTENT_MANY,
-                         ids=lambda c: "tiledp," + ",".join(map(str, c[0])) + f"-{c[1]}-kps{c[2]}")
+                         ids=lambda c: f"{c[0]}:tiledp," + ",".join(map(str, c[1])) + f"-{c[2]}-kps{c[3]}")
 def test_persistent_many_tiles_exact(hip_lib, case):
-    cfg, dtype, kps = case
+    layout, cfg, dtype, kps = case
     bm, bn = cfg[0], cfg[1]
     M, N, S = 2048, 16 * 256 + 40, 8
     K = (S - 1) * kps + 64
     plan = _plan_text("tiledp", cfg)
-    text = hip_lib.describe_planned(plan, M, N, K, kps, S, inputs.DTYPES[dtype])
-    print(f"case {dtype} M{M} N{N} K{K} kps{kps} S{S}: {text}", flush=True)
+    text = hip_lib.describe_planned(plan, M, N, K, kps, S, inputs.DTYPES[dtype], layout=layout)
+    print(f"case {layout} {dtype} M{M} N{N} K{K} kps{kps} S{S}: {text}", flush=True)
     assert text.endswith("grid256 persistent"), text
+    stored = (lambda t: t) if layout == "nk" else (lambda t: t.T.contiguous())
     dev = torch.device("cuda:0")
     ea, eb = inputs.exact_operands(M, N, K, dtype, seed=bm + bn + kps)
     ea64 = oracle.decode(inputs.stored_bits(ea), dtype)
@@ -267,8 +274,8 @@ def test_persistent_many_tiles_exact(hip_lib, case):
     for poison in ("nan", "seven"):
         pbuf = inputs.guarded_buffer(S * M * N, poison).to(dev)
         cbuf = inputs.guarded_buffer(M * N, poison).to(dev)
-        hip_lib.gemm_planned(plan, ea.to(dev), eb.to(dev), pbuf[: S * M * N].view(S, M, N), kps, S,
-                             C=cbuf[: M * N].view(M, N))
+        hip_lib.gemm_planned(plan, ea.to(dev), stored(eb).to(dev), pbuf[: S * M * N].view(S, M, N), kps, S,
+                             C=cbuf[: M * N].view(M, N), layout=layout)
         torch.cuda.synchronize()
         p, c = pbuf.cpu().numpy(), cbuf.cpu().numpy()
         assert np.all(p[S * M * N:].view(np.uint32) == guard)

@@ -284,7 +284,7 @@ int splitk_describe_bn(int64_t M, int64_t N, int64_t K, int64_t k_per_split, int
  *            "tiledp,BM,BN,WM,WN"            persistent large-tile kernel:
  *                                             at most one workgroup per CU,
  *                                             each walking several tiles
- *                                             (B [N,K] only)
+ *                                             (B [K,N]: 256x256 only)
  *          naming an instantiated configuration (the lists in gemm_bt.hip).
  * Every check of splitk_gemm_bt applies first.  Returns SPLITK_ERR_NULL for a
  * NULL plan, SPLITK_ERR_PLAN (nothing launched) if the text names no

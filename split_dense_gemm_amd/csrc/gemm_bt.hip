@@ -45,6 +45,10 @@
 //    that the slab sum can read the slabs from the L2 that holds them.
 //  * Slabs too large for the memory-side cache are stored as streaming
 //    writes (stream_slabs).
+//
+// Which kernel and configuration serves a problem (the shape rules, the tile
+// order, the persistent form) is decided in plan.cpp; this file holds the
+// kernels, their launchers and the lists of instantiated configurations.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdio.h>

@@ -41,6 +41,30 @@ def _cases(n=60, seed=20261202):
     return out
 
 
+def _large_cases(n=20, seed=20261203):
+    """Geometries for the large-tile kernels: M a multiple of 256 up to 2048,
+    N from ~1900 to ~4200 (mostly not a multiple of 256), K up to 2080, 3-8
+    splits,
+    so that the draws reach the one-tile 256x128 and 256x256 kernels, their
+    persistent form (more 256x256 tiles than CUs), narrowed last column
+    tiles and the split-fastest order of one-round grids, in both layouts."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        layout = "kn" if rng.random() < 0.4 else "nk"
+        M = 256 * int(rng.integers(2, 9))
+        N = 8 * int(rng.integers(250, 525)) if layout == "kn" else int(rng.integers(1900, 4200))
+        S = int(rng.integers(3, 9))
+        K = 32 * int(rng.integers(2 * S, 66))
+        kps = 32 * -(-(K // 32) // S)
+        while (S - 1) * kps >= K:
+            S -= 1
+        dtype = ["f32", "f16", "bf16", "bf16"][int(rng.integers(0, 4))]
+        out_t = ["f32", "f32", "f16", "bf16"][int(rng.integers(0, 4))]
+        out.append((100 + i, layout, M, N, K, kps, S, dtype, out_t))
+    return out
+
+
 @pytest.fixture(scope="module")
 def sdg(hip_lib):
     if not torch.cuda.is_available():
@@ -52,7 +76,7 @@ def _vals(t):
     return oracle.decode(inputs.stored_bits(t), inputs.dtype_name(t))
 
 
-@pytest.mark.parametrize("case", _cases(), ids=lambda c: "r{}-{}-{}x{}x{}-s{}-{}-{}".format(
+@pytest.mark.parametrize("case", _cases() + _large_cases(), ids=lambda c: "r{}-{}-{}x{}x{}-s{}-{}-{}".format(
     c[0], c[1], c[2], c[3], c[4], c[6], c[7], c[8]))
 def test_random_geometry(sdg, case):
     i, layout, M, N, K, kps, S, dtype, out_t = case
